@@ -1,0 +1,240 @@
+// C ABI of the MoE library: argument checks, workspace layout, tile-class choice and the
+// launch sequence route -> Linear1(+SwiGLU+requant) -> Linear2(+weights) -> combine.
+// Everything is enqueued on the caller's stream; nothing here synchronises except
+// moe_read_diagnostics, and nothing allocates device memory.
+#include <cstring>
+
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kMaxBlockM = 256;
+constexpr int kMinBlockM = 64;
+
+bool shape_ok(const moe_shape_t* s) {
+    if (!s) return false;
+    if (s->num_experts < 1 || s->num_experts > MOE_MAX_EXPERTS) return false;
+    if (s->hidden < 256 || s->hidden % 256 != 0) return false;
+    if (s->intermediate < 128 || s->intermediate % 128 != 0) return false;
+    if (s->num_topk < 1 || s->num_topk > MOE_MAX_TOPK || s->num_topk > s->num_experts) return false;
+    if (s->max_tokens < 0) return false;
+    const uint64_t slots = (uint64_t)s->max_tokens * (uint64_t)s->num_topk;
+    if (slots >= (1ull << 31)) return false;
+    const uint64_t ppad = slots + (uint64_t)s->num_experts * (kMaxBlockM - 1);
+    // 32-bit row offsets inside the GEMM kernels
+    if ((uint64_t)s->max_tokens * (uint64_t)s->hidden >= (1ull << 32)) return false;
+    if (ppad * (uint64_t)s->intermediate >= (1ull << 32)) return false;
+    return true;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int choose_block_m(const moe_shape_t& s, int T) {
+    const long avg = (long)T * s.num_topk / s.num_experts;
+    if (avg >= 512) return 256;
+    if (avg >= 128) return 128;
+    return 64;
+}
+
+struct WsLayout {
+    moe_layout_t pub;
+    size_t blk;        // i32 [nblk * E] chunk histograms, then i32 [nblk] invalid counts
+    int max_pad_rows;
+};
+
+WsLayout ws_layout(const moe_shape_t& s) {
+    WsLayout w{};
+    const size_t E = s.num_experts, H = s.hidden, I = s.intermediate;
+    const size_t slots = (size_t)s.max_tokens * s.num_topk;
+    const size_t nblk = (slots + kRouteChunk - 1) / kRouteChunk;
+    const size_t ppad = slots + E * (kMaxBlockM - 1);
+    const size_t max_tiles = (slots + kMinBlockM - 1) / kMinBlockM + E;
+    const size_t sfs = 4 * ((I + 511) / 512);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off = align_up(off + bytes, 256);
+        return o;
+    };
+    w.pub.meta = take(8 * sizeof(int32_t));
+    w.pub.counts = take(E * sizeof(int32_t));
+    w.pub.offsets = take((E + 1) * sizeof(int32_t));
+    w.blk = take((nblk * E + nblk) * sizeof(int32_t));
+    w.pub.perm = take(ppad * sizeof(int32_t));
+    w.pub.inv = take(slots * sizeof(int32_t));
+    w.pub.tile_expert = take(max_tiles * sizeof(int32_t));
+    w.pub.tile_row0 = take(max_tiles * sizeof(int32_t));
+    w.pub.h8 = take(ppad * I);
+    w.pub.h_sf = take(ppad * sfs);
+    w.pub.h_sf_stride = sfs;
+    w.pub.stage = take(slots * H * sizeof(uint16_t));
+    w.pub.total = off;
+    w.pub.max_tiles = (int32_t)max_tiles;
+    w.max_pad_rows = (int)ppad;
+    return w;
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+int moe_version(void) { return 10000; }
+
+const char* moe_status_string(int status) {
+    switch (status) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_NULL: return "null pointer";
+        case MOE_ERR_SHAPE: return "unsupported shape";
+        case MOE_ERR_ALIGN: return "pointer not 16-byte aligned";
+        case MOE_ERR_WORKSPACE: return "buffer too small";
+        case MOE_ERR_TOKENS: return "num_tokens out of range";
+        case MOE_ERR_HIP: return "HIP error";
+        default: return "unknown status";
+    }
+}
+
+size_t moe_packed_weights_bytes(const moe_shape_t* shape) {
+    if (!shape_ok(shape)) return 0;
+    return packed_layout(*shape).total;
+}
+
+size_t moe_workspace_bytes(const moe_shape_t* shape) {
+    if (!shape_ok(shape)) return 0;
+    return ws_layout(*shape).pub.total;
+}
+
+int moe_workspace_layout(const moe_shape_t* shape, int32_t num_tokens, moe_layout_t* out) {
+    if (!out || !shape) return MOE_ERR_NULL;
+    if (!shape_ok(shape)) return MOE_ERR_SHAPE;
+    if (num_tokens < 0 || num_tokens > shape->max_tokens) return MOE_ERR_TOKENS;
+    WsLayout w = ws_layout(*shape);
+    w.pub.block_m = choose_block_m(*shape, num_tokens);
+    *out = w.pub;
+    return MOE_OK;
+}
+
+int moe_prepare_weights(const moe_shape_t* shape, const uint8_t* w1, const uint8_t* w1_sf,
+                        const uint8_t* w2, const uint8_t* w2_sf, void* packed,
+                        size_t packed_bytes, hipStream_t stream) {
+    if (!shape || !w1 || !w1_sf || !w2 || !w2_sf || !packed) return MOE_ERR_NULL;
+    if (!shape_ok(shape)) return MOE_ERR_SHAPE;
+    if (!aligned16(w1) || !aligned16(w1_sf) || !aligned16(w2) || !aligned16(w2_sf) ||
+        !aligned16(packed))
+        return MOE_ERR_ALIGN;
+    const PackedLayout L = packed_layout(*shape);
+    if (packed_bytes < L.total) return MOE_ERR_WORKSPACE;
+    if (launch_pack(*shape, L, w1, w1_sf, w2, w2_sf, static_cast<uint8_t*>(packed), stream) !=
+        hipSuccess)
+        return MOE_ERR_HIP;
+    return MOE_OK;
+}
+
+int moe_forward(uint16_t* y_bf16, const uint8_t* x_fp8, const uint8_t* x_sf,
+                const int32_t* topk_idx, const float* topk_weights, int32_t num_tokens,
+                const moe_shape_t* shape, const void* packed, void* workspace,
+                size_t workspace_bytes, hipStream_t stream) {
+    if (!shape) return MOE_ERR_NULL;
+    if (!shape_ok(shape)) return MOE_ERR_SHAPE;
+    if (num_tokens < 0 || num_tokens > shape->max_tokens) return MOE_ERR_TOKENS;
+    if (!y_bf16 || !x_fp8 || !x_sf || !topk_idx || !topk_weights || !packed || !workspace)
+        return MOE_ERR_NULL;
+    if (!aligned16(y_bf16) || !aligned16(x_fp8) || !aligned16(x_sf) || !aligned16(topk_idx) ||
+        !aligned16(topk_weights) || !aligned16(packed) || !aligned16(workspace))
+        return MOE_ERR_ALIGN;
+    const WsLayout W = ws_layout(*shape);
+    if (workspace_bytes < W.pub.total) return MOE_ERR_WORKSPACE;
+    if (num_tokens == 0) return MOE_OK;
+
+    const moe_shape_t& s = *shape;
+    const int T = num_tokens, E = s.num_experts, H = s.hidden, I = s.intermediate, k = s.num_topk;
+    const int BM = choose_block_m(s, T);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    auto i32 = [&](size_t off) { return reinterpret_cast<int32_t*>(ws + off); };
+    int32_t* meta = i32(W.pub.meta);
+    int32_t* perm = i32(W.pub.perm);
+    int32_t* tile_e = i32(W.pub.tile_expert);
+    int32_t* tile_r = i32(W.pub.tile_row0);
+
+    if (launch_route(topk_idx, T * k, E, BM, i32(W.blk), meta, i32(W.pub.counts),
+                     i32(W.pub.offsets), perm, i32(W.pub.inv), tile_e, tile_r, W.pub.max_tiles,
+                     stream) != hipSuccess)
+        return MOE_ERR_HIP;
+
+    const PackedLayout L = packed_layout(s);
+    const uint8_t* pk = static_cast<const uint8_t*>(packed);
+    // The grid covers every tile the routing of T tokens can produce.
+    const int tiles_bound = (T * k + BM - 1) / BM + E;
+    const int max_tiles = tiles_bound < W.pub.max_tiles ? tiles_bound : W.pub.max_tiles;
+
+    GemmArgs a1{};
+    a1.a = x_fp8;
+    a1.a_sf = x_sf;
+    a1.a_stride = H;
+    a1.a_sf_stride = 4 * ((H + 511) / 512);
+    a1.K = H;
+    a1.topk = k;
+    a1.perm = perm;
+    a1.meta = meta;
+    a1.tile_expert = tile_e;
+    a1.tile_row0 = tile_r;
+    a1.n_tiles = I / 128;
+    a1.max_tiles = max_tiles;
+    a1.b = pk + L.w1d;
+    a1.b_sf = reinterpret_cast<const uint32_t*>(pk + L.w1s);
+    a1.b_expert = L.w1d_expert;
+    a1.b_ntile = L.w1d_ntile;
+    a1.bs_expert = L.w1s_expert / 4;
+    a1.bs_ntile = L.w1s_ntile / 4;
+    a1.h8 = ws + W.pub.h8;
+    a1.h_sf = ws + W.pub.h_sf;
+    a1.h_stride = I;
+    a1.h_sf_stride = (int)W.pub.h_sf_stride;
+    if (launch_linear1(BM, a1, stream) != hipSuccess) return MOE_ERR_HIP;
+
+    GemmArgs a2 = a1;
+    a2.a = ws + W.pub.h8;
+    a2.a_sf = ws + W.pub.h_sf;
+    a2.a_stride = I;
+    a2.a_sf_stride = (int)W.pub.h_sf_stride;
+    a2.K = I;
+    a2.n_tiles = H / 256;
+    a2.b = pk + L.w2d;
+    a2.b_sf = reinterpret_cast<const uint32_t*>(pk + L.w2s);
+    a2.b_expert = L.w2d_expert;
+    a2.b_ntile = L.w2d_ntile;
+    a2.bs_expert = L.w2s_expert / 4;
+    a2.bs_ntile = L.w2s_ntile / 4;
+    a2.stage = reinterpret_cast<uint16_t*>(ws + W.pub.stage);
+    a2.topk_weights = topk_weights;
+    a2.out_cols = H;
+    if (launch_linear2(BM, a2, stream) != hipSuccess) return MOE_ERR_HIP;
+
+    if (launch_combine(reinterpret_cast<const uint16_t*>(ws + W.pub.stage), topk_idx, T, k, E, H,
+                       y_bf16, stream) != hipSuccess)
+        return MOE_ERR_HIP;
+    return MOE_OK;
+}
+
+int moe_read_diagnostics(const moe_shape_t* shape, const void* workspace, int32_t* invalid_ids,
+                         int32_t* counts_out, hipStream_t stream) {
+    if (!shape || !workspace || !invalid_ids) return MOE_ERR_NULL;
+    if (!shape_ok(shape)) return MOE_ERR_SHAPE;
+    const WsLayout W = ws_layout(*shape);
+    const uint8_t* ws = static_cast<const uint8_t*>(workspace);
+    if (hipStreamSynchronize(stream) != hipSuccess) return MOE_ERR_HIP;
+    int32_t meta[8];
+    if (hipMemcpy(meta, ws + W.pub.meta, sizeof(meta), hipMemcpyDeviceToHost) != hipSuccess)
+        return MOE_ERR_HIP;
+    *invalid_ids = meta[1];
+    if (counts_out &&
+        hipMemcpy(counts_out, ws + W.pub.counts, sizeof(int32_t) * shape->num_experts,
+                  hipMemcpyDeviceToHost) != hipSuccess)
+        return MOE_ERR_HIP;
+    return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,91 @@
+// Internal declarations shared by the HIP sources of the MoE library (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstddef>
+#include <cstdint>
+
+#include "moe.h"
+
+namespace moe {
+
+// Routing processes the flattened (token, slot) list in chunks of this many slots per
+// workgroup; each chunk's per-expert histogram is one row of the block-count table.
+constexpr int kRouteChunk = 4096;
+constexpr int kRouteThreads = 256;
+// Output columns of one grouped-GEMM tile: Linear1 = 128 gate + 128 up columns of one
+// 128-wide block of the intermediate; Linear2 = 256 hidden columns.
+constexpr int kBN = 256;
+// One K step of the main loop (one 16x16x128 scaled MFMA along K).
+constexpr int kBK = 128;
+// Bytes of one packed B fragment: 16 columns x 128 K of FP4 = 64 lanes x 16 bytes.
+constexpr int kFragBytes = 1024;
+// Bytes of the packed B data of one (tile, K step): 16 fragments.
+constexpr int kBTileBytes = 16 * kFragBytes;
+// Bytes of the packed B scales of one (tile, 512-K block): 16 fragments x 64 lanes x 4.
+constexpr int kBScaleBlockBytes = 16 * 64 * 4;
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+inline int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+// Offsets of the four regions of the packed weight buffer.
+struct PackedLayout {
+    size_t w1d, w1s, w2d, w2s, total;
+    size_t w1d_expert, w1d_ntile;   // bytes per expert, per 128-column block of I
+    size_t w1s_expert, w1s_ntile;
+    size_t w2d_expert, w2d_ntile;   // per 256-column block of H
+    size_t w2s_expert, w2s_ntile;
+};
+
+PackedLayout packed_layout(const moe_shape_t& s);
+
+// Routing kernels (route.hip)
+hipError_t launch_route(const int32_t* topk_idx, int num_slots, int E, int block_m,
+                        int32_t* blk_counts, int32_t* meta, int32_t* counts, int32_t* offsets,
+                        int32_t* perm, int32_t* inv, int32_t* tile_expert, int32_t* tile_row0,
+                        int max_tiles, hipStream_t stream);
+
+// Weight transform (pack.hip)
+hipError_t launch_pack(const moe_shape_t& s, const PackedLayout& L,
+                       const uint8_t* w1, const uint8_t* w1_sf, const uint8_t* w2,
+                       const uint8_t* w2_sf, uint8_t* packed, hipStream_t stream);
+
+// Grouped GEMMs (gemm.hip)
+struct GemmArgs {
+    // A operand: rows of FP8 codes with per-1x128 UE8M0 scales
+    const uint8_t* a;          // x_fp8 (Linear1, gathered through perm) or h8 (Linear2)
+    const uint8_t* a_sf;
+    int a_stride;              // bytes per A row (= K)
+    int a_sf_stride;           // bytes per A scale row
+    int K;                     // reduction length (multiple of 128)
+    int topk;                  // Linear1: slot -> token = slot / topk
+    const int32_t* perm;
+    const int32_t* meta;       // meta[0] = number of M tiles in use
+    const int32_t* tile_expert;
+    const int32_t* tile_row0;
+    int n_tiles;               // column tiles per M tile
+    int max_tiles;
+    // B operand: packed weights
+    const uint8_t* b;
+    const uint32_t* b_sf;
+    size_t b_expert, b_ntile;        // bytes
+    size_t bs_expert, bs_ntile;      // 32-bit words
+    // Linear1 outputs
+    uint8_t* h8;
+    uint8_t* h_sf;
+    int h_stride;              // = I
+    int h_sf_stride;
+    // Linear2 outputs
+    uint16_t* stage;
+    const float* topk_weights;
+    int out_cols;              // = H
+};
+
+hipError_t launch_linear1(int block_m, const GemmArgs& a, hipStream_t stream);
+hipError_t launch_linear2(int block_m, const GemmArgs& a, hipStream_t stream);
+
+// Combine (combine.hip)
+hipError_t launch_combine(const uint16_t* stage, const int32_t* topk_idx, int T, int k, int E,
+                          int H, uint16_t* y, hipStream_t stream);
+
+}  // namespace moe

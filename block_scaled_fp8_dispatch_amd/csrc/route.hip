@@ -1,0 +1,184 @@
+// Dispatch for the one-GPU MoE forward: per-expert histogram, block-aligned exclusive
+// scan, stable permutation of the (token, slot) assignments, inverse map and tile list.
+//
+// The explainer (chenxutan.com/d/1930 section 3.1, step 1) describes dispatch as moving
+// each token to its experts' regions; the contiguous-layout grouped GEMM
+// (juejin.cn/post/7631516744872673307, "MoE模型专属优化") keeps every expert's rows
+// together with each group block-aligned. Here only indices move: the GEMM gathers the
+// activation rows through `perm`.
+//
+// Three launches, all deterministic:
+//   count   one workgroup per chunk of kRouteChunk slots: per-expert histogram of the
+//           chunk (LDS integer atomics; the count does not depend on their order) and
+//           the chunk's number of invalid ids
+//   scan    one workgroup: expert totals, per-chunk bases, padded offsets, tile list,
+//           padding rows of perm set to -1, invalid-id total
+//   scatter one workgroup per chunk: the stable rank of each slot among the chunk's
+//           slots of the same expert (wave ballots), then perm / inv
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kMaxE = MOE_MAX_EXPERTS;
+constexpr int kSlotsPerThread = kRouteChunk / kRouteThreads;
+
+__global__ __launch_bounds__(kRouteThreads) void route_count_kernel(
+    const int32_t* __restrict__ idx, int num_slots, int E, int32_t* __restrict__ blk_counts,
+    int32_t* __restrict__ blk_invalid) {
+    __shared__ int hist[kMaxE];
+    __shared__ int invalid;
+    const int tid = threadIdx.x;
+    for (int e = tid; e < E; e += kRouteThreads) hist[e] = 0;
+    if (tid == 0) invalid = 0;
+    __syncthreads();
+    const int base = blockIdx.x * kRouteChunk;
+    int my_invalid = 0;
+    for (int i = 0; i < kSlotsPerThread; ++i) {
+        const int s = base + i * kRouteThreads + tid;
+        if (s < num_slots) {
+            const int e = idx[s];
+            if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
+            else if (e != -1) ++my_invalid;
+        }
+    }
+    if (my_invalid) atomicAdd(&invalid, my_invalid);
+    __syncthreads();
+    for (int e = tid; e < E; e += kRouteThreads) blk_counts[(size_t)blockIdx.x * E + e] = hist[e];
+    if (tid == 0) blk_invalid[blockIdx.x] = invalid;
+}
+
+// One workgroup of up to 1024 threads; thread e owns expert e.
+__global__ __launch_bounds__(1024) void route_scan_kernel(
+    int32_t* __restrict__ blk_counts, const int32_t* __restrict__ blk_invalid, int nblk, int E,
+    int block_m, int32_t* __restrict__ meta, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ tile_expert,
+    int32_t* __restrict__ tile_row0, int max_tiles) {
+    __shared__ int padded[1024];
+    __shared__ int warp_sums[16];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    int c = 0;
+    if (tid < E) {
+        // per-chunk bases within the expert, in chunk order (exclusive prefix)
+        for (int b = 0; b < nblk; ++b) {
+            int* p = blk_counts + (size_t)b * E + tid;
+            const int v = *p;
+            *p = c;
+            c += v;
+        }
+    }
+    const int pad = (c + block_m - 1) / block_m * block_m;
+    // exclusive scan of `pad` over threads 0..1023 (experts in order)
+    int incl = pad;
+    for (int d = 1; d < 64; d <<= 1) {
+        const int t = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += t;
+    }
+    if (lane == 63) warp_sums[wave] = incl;
+    __syncthreads();
+    int wave_base = 0;
+    for (int w = 0; w < wave; ++w) wave_base += warp_sums[w];
+    const int excl = wave_base + incl - pad;
+    padded[tid] = excl;
+    __syncthreads();
+    if (tid < E) {
+        counts[tid] = c;
+        offsets[tid] = excl;
+        if (tid == E - 1) offsets[E] = excl + pad;
+        for (int r = excl + c; r < excl + pad; ++r) perm[r] = -1;
+        for (int r = excl; r < excl + pad; r += block_m) {
+            const int t = r / block_m;
+            if (t < max_tiles) {
+                tile_expert[t] = tid;
+                tile_row0[t] = r;
+            }
+        }
+    }
+    if (tid == 0) {
+        int inv = 0;
+        for (int b = 0; b < nblk; ++b) inv += blk_invalid[b];
+        int total = 0;
+        for (int w = 0; w < 16; ++w) total += warp_sums[w];
+        meta[0] = total / block_m;
+        meta[1] = inv;
+        meta[2] = block_m;
+    }
+}
+
+__global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(
+    const int32_t* __restrict__ idx, int num_slots, int E, int nbits,
+    const int32_t* __restrict__ blk_base, const int32_t* __restrict__ offsets,
+    int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+    __shared__ int base[kMaxE];      // offsets[e] + rows of e in earlier chunks
+    __shared__ int running[kMaxE];   // rows of e in earlier rounds of this chunk
+    __shared__ int wave_cnt[kRouteThreads / 64][kMaxE];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    for (int e = tid; e < E; e += kRouteThreads) {
+        base[e] = offsets[e] + blk_base[(size_t)blockIdx.x * E + e];
+        running[e] = 0;
+        for (int w = 0; w < kRouteThreads / 64; ++w) wave_cnt[w][e] = 0;
+    }
+    __syncthreads();
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int chunk0 = blockIdx.x * kRouteChunk;
+    for (int round = 0; round < kSlotsPerThread; ++round) {
+        const int s = chunk0 + round * kRouteThreads + tid;
+        const bool in_range = s < num_slots;
+        const int e = in_range ? idx[s] : -1;
+        const bool ok = e >= 0 && e < E;
+        // lanes of this wave holding the same expert id
+        uint64_t peers = __ballot(ok);
+        for (int b = 0; b < nbits; ++b) {
+            const bool bit = (e >> b) & 1;
+            const uint64_t bal = __ballot(bit);
+            peers &= bit ? bal : ~bal;
+        }
+        const int rank_w = __popcll(peers & lt_mask);
+        const int cnt = __popcll(peers);
+        if (ok && rank_w == cnt - 1) wave_cnt[wave][e] = cnt;
+        __syncthreads();
+        if (ok) {
+            int before = running[e];
+            for (int w = 0; w < wave; ++w) before += wave_cnt[w][e];
+            const int pos = base[e] + before + rank_w;
+            perm[pos] = s;
+            inv[s] = pos;
+        } else if (in_range) {
+            inv[s] = -1;
+        }
+        __syncthreads();
+        for (int x = tid; x < E; x += kRouteThreads) {
+            int add = 0;
+            for (int w = 0; w < kRouteThreads / 64; ++w) {
+                add += wave_cnt[w][x];
+                wave_cnt[w][x] = 0;
+            }
+            running[x] += add;
+        }
+        __syncthreads();
+    }
+}
+
+}  // namespace
+
+hipError_t launch_route(const int32_t* topk_idx, int num_slots, int E, int block_m,
+                        int32_t* blk_counts, int32_t* meta, int32_t* counts, int32_t* offsets,
+                        int32_t* perm, int32_t* inv, int32_t* tile_expert, int32_t* tile_row0,
+                        int max_tiles, hipStream_t stream) {
+    const int nblk = cdiv(num_slots, kRouteChunk);
+    int32_t* blk_invalid = blk_counts + (size_t)nblk * E;
+    int nbits = 1;
+    while ((1 << nbits) < E) ++nbits;
+    route_count_kernel<<<nblk, kRouteThreads, 0, stream>>>(topk_idx, num_slots, E, blk_counts,
+                                                            blk_invalid);
+    route_scan_kernel<<<1, 1024, 0, stream>>>(blk_counts, blk_invalid, nblk, E, block_m, meta,
+                                              counts, offsets, perm, tile_expert, tile_row0,
+                                              max_tiles);
+    route_scatter_kernel<<<nblk, kRouteThreads, 0, stream>>>(topk_idx, num_slots, E, nbits,
+                                                              blk_counts, offsets, perm, inv);
+    return hipGetLastError();
+}
+
+}  // namespace moe

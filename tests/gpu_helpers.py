@@ -1,0 +1,107 @@
+"""Helpers for the GPU tests: run the HIP path through the C ABI and fetch what the
+workspace holds, and compare with the oracle under the stated acceptance rules."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import block_scaled_fp8_dispatch_amd as moe
+import oracle
+
+Y_TOL = 2e-2            # max |y_gpu - y_ref| / max |y_ref| per row
+OFF_BY_ONE_MAX = 1e-3   # fraction of requantised FP8 intermediates one code off
+
+
+class Run:
+    """One prepared problem on the GPU (packed weights + workspace) and its last forward."""
+
+    def __init__(self, inp, max_tokens=None, device="cuda"):
+        cfg = inp.cfg
+        self.inp = inp
+        self.T = inp.x_fp8.shape[0]
+        self.shape = moe.make_shape(cfg.E, cfg.H, cfg.I, cfg.k, max_tokens or max(self.T, 1))
+        nb = moe.moe_packed_weights_bytes(self.shape)
+        assert nb > 0
+        self.packed = torch.empty(nb, dtype=torch.uint8, device=device)
+        moe.moe_prepare_weights(self.shape, inp.w1, inp.w1_sf, inp.w2, inp.w2_sf, self.packed)
+        self.ws = torch.empty(moe.moe_workspace_bytes(self.shape), dtype=torch.uint8, device=device)
+        self.y = torch.empty(max(self.T, 1), cfg.H, dtype=torch.int16, device=device)
+
+    def forward(self, T=None, poison=True):
+        T = self.T if T is None else T
+        if poison:
+            self.ws.fill_(0xFF)
+            self.y.fill_(0x7FBF)
+        moe.moe_forward(self.y, self.inp.x_fp8, self.inp.x_sf, self.inp.topk_idx,
+                        self.inp.topk_weights, T, self.shape, self.packed, self.ws)
+        torch.cuda.synchronize()
+        return self.y[:T].cpu().numpy().view(np.uint16)
+
+    def layout(self, T=None):
+        return moe.moe_workspace_layout(self.shape, self.T if T is None else T)
+
+    def ws_i32(self, off, n):
+        return self.ws[off: off + 4 * n].cpu().numpy().view(np.int32).copy()
+
+    def routing(self, T=None):
+        T = self.T if T is None else T
+        L = self.layout(T)
+        E, k = self.shape.num_experts, self.shape.num_topk
+        meta = self.ws_i32(L["meta"], 8)
+        offsets = self.ws_i32(L["offsets"], E + 1)
+        ntiles = int(meta[0])
+        return dict(
+            block_m=L["block_m"], meta=meta,
+            counts=self.ws_i32(L["counts"], E), offsets=offsets,
+            perm=self.ws_i32(L["perm"], int(offsets[E])), inv=self.ws_i32(L["inv"], T * k),
+            tile_expert=self.ws_i32(L["tile_expert"], ntiles),
+            tile_row0=self.ws_i32(L["tile_row0"], ntiles), num_invalid=meta[1])
+
+    def intermediates(self, rows):
+        """h8 codes [len(rows), I] and h_sf bytes [len(rows), I/128] of the given perm rows."""
+        L = self.layout()
+        I = self.shape.intermediate
+        sfs = L["h_sf_stride"]
+        n = int(np.max(rows)) + 1
+        rt = torch.as_tensor(np.asarray(rows, dtype=np.int64), device=self.ws.device)
+        h8 = self.ws[L["h8"]: L["h8"] + n * I].view(n, I)[rt].cpu().numpy()
+        hs = self.ws[L["h_sf"]: L["h_sf"] + n * sfs].view(n, sfs)[rt][:, : I // 128].cpu().numpy()
+        return h8, hs
+
+
+def check_routing(got: dict, idx_np: np.ndarray, E: int):
+    ref = oracle.route(idx_np, E, got["block_m"])
+    for key in ("counts", "offsets", "perm", "inv", "tile_expert", "tile_row0"):
+        assert np.array_equal(got[key], ref[key]), f"routing field {key} differs"
+    assert int(got["num_invalid"]) == int(ref["num_invalid"])
+    return ref
+
+
+def check_intermediates(run: Run, ref: dict, inv: np.ndarray):
+    """Compare GPU h8/h_sf with the oracle's requantised intermediate slot by slot."""
+    slots = sorted(ref["h8"].keys())
+    if not slots:
+        return 0.0
+    rows = inv[np.array(slots)]
+    assert np.all(rows >= 0)
+    g8, gsf = run.intermediates(rows)
+    r8 = np.stack([ref["h8"][s] for s in slots])
+    rsf = np.stack([ref["h_sf"][s] for s in slots])
+    I = r8.shape[1]
+    gs = np.repeat(gsf, 128, axis=1)
+    rs = np.repeat(rsf, 128, axis=1)
+    dist = oracle.e4m3_code_distance(g8, gs, r8, rs)
+    frac = float((dist > 0).mean())
+    assert dist.max() <= 1, f"intermediate off by {dist.max()} codes"
+    assert frac <= OFF_BY_ONE_MAX, f"{frac:.2e} of intermediates off by one code"
+    return frac
+
+
+def check_y(y_bits: np.ndarray, ref: dict, tokens=None, cols=None):
+    yg = y_bits if tokens is None else y_bits[np.asarray(tokens)]
+    if cols is not None:
+        yg = yg[:, np.asarray(cols)]
+    err = oracle.y_row_error(yg, ref["y"])
+    assert np.all(np.isfinite(err)), "a row the oracle gives as exactly 0 is non-zero"
+    assert err.max() <= Y_TOL, f"max row error {err.max():.3e}"
+    return float(err.max())

@@ -1,0 +1,112 @@
+"""The C-ABI library: it loads, exports every symbol include/moe.h declares, and rejects bad
+arguments on the host before launching anything (no GPU needed: no call below reaches
+the device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_scaled_fp8_dispatch_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_functions():
+    text = open(os.path.join(ROOT, "include", "moe.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text))
+    return names
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(moe.LIB_PATH):
+        pytest.fail("libmoe.so is not built (run __graft_entry__.build())")
+    return moe.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _header_functions()
+    assert declared == set(moe.EXPORTED), declared ^ set(moe.EXPORTED)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert moe.moe_version() >= 10000
+    assert moe.moe_status_string(moe.MOE_OK) == "ok"
+    assert "align" in moe.moe_status_string(moe.MOE_ERR_ALIGN)
+    assert moe.moe_status_string(12345) == "unknown status"
+
+
+def test_sizes_and_shape_validation(lib):
+    good = moe.make_shape(8, 7168, 18432, 2, 8192)
+    assert moe.moe_packed_weights_bytes(good) == 8 * (2 * 18432 * 7168 // 2 + 2 * 18432 * 7168 // 32
+                                                      + 7168 * 18432 // 2 + 7168 * 18432 // 32)
+    assert moe.moe_workspace_bytes(good) > 8192 * 2 * 7168 * 2
+    for bad in (moe.make_shape(0, 256, 128, 1, 1), moe.make_shape(4, 200, 128, 1, 1),
+                moe.make_shape(4, 256, 100, 1, 1), moe.make_shape(4, 256, 128, 5, 1),
+                moe.make_shape(4, 256, 128, 0, 1), moe.make_shape(4, 256, 128, 1, -1),
+                moe.make_shape(2000, 256, 128, 1, 1), moe.make_shape(4, 256, 128, 65, 100)):
+        assert moe.moe_packed_weights_bytes(bad) == 0
+        assert moe.moe_workspace_bytes(bad) == 0
+
+
+def test_layout_is_consistent(lib):
+    s = moe.make_shape(32, 7168, 2048, 8, 4096)
+    L = moe.moe_workspace_layout(s, 4096)
+    assert L["total"] == moe.moe_workspace_bytes(s)
+    assert L["block_m"] == 256
+    assert moe.moe_workspace_layout(s, 128)["block_m"] == 64
+    offs = [L[k] for k in ("meta", "counts", "offsets", "perm", "inv", "tile_expert", "tile_row0",
+                           "h8", "h_sf", "stage")]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    assert L["h_sf_stride"] == 4 * ((2048 + 511) // 512)
+    with pytest.raises(moe.MoEError):
+        moe.moe_workspace_layout(s, 4097)
+
+
+def test_forward_host_errors(lib):
+    s = moe.make_shape(4, 256, 512, 2, 64)
+    ws_bytes = moe.moe_workspace_bytes(s)
+    A = 0x10000  # aligned fake addresses: every case below returns before touching them
+    args = dict(y=A, x=A, xsf=A, idx=A, w=A, packed=A, ws=A)
+
+    def call(T=64, shape=s, wsb=ws_bytes, **over):
+        a = dict(args, **over)
+        return moe.moe_forward_raw(a["y"], a["x"], a["xsf"], a["idx"], a["w"], T, shape,
+                                   a["packed"], a["ws"], wsb, None)
+
+    assert call(y=None) == moe.MOE_ERR_NULL
+    assert call(idx=None) == moe.MOE_ERR_NULL
+    assert call(ws=None) == moe.MOE_ERR_NULL
+    assert call(x=A + 8) == moe.MOE_ERR_ALIGN
+    assert call(w=A + 4) == moe.MOE_ERR_ALIGN
+    assert call(wsb=ws_bytes - 1) == moe.MOE_ERR_WORKSPACE
+    assert call(T=65) == moe.MOE_ERR_TOKENS
+    assert call(T=-1) == moe.MOE_ERR_TOKENS
+    assert call(shape=moe.make_shape(4, 250, 512, 2, 64)) == moe.MOE_ERR_SHAPE
+    assert call(T=0) == moe.MOE_OK    # nothing to do: no launch
+
+
+def test_prepare_host_errors(lib):
+    s = moe.make_shape(4, 256, 512, 2, 64)
+    nb = moe.moe_packed_weights_bytes(s)
+    A = 0x10000
+    assert moe.moe_prepare_weights_raw(s, None, A, A, A, A, nb, None) == moe.MOE_ERR_NULL
+    assert moe.moe_prepare_weights_raw(s, A, A + 1, A, A, A, nb, None) == moe.MOE_ERR_ALIGN
+    assert moe.moe_prepare_weights_raw(s, A, A, A, A, A, nb - 1, None) == moe.MOE_ERR_WORKSPACE
+    bad = moe.make_shape(4, 256, 100, 2, 64)
+    assert moe.moe_prepare_weights_raw(bad, A, A, A, A, A, nb, None) == moe.MOE_ERR_SHAPE
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    from block_scaled_fp8_dispatch_amd import _lib
+    saved = _lib._lib
+    try:
+        _lib._lib = None
+        with pytest.raises(ImportError):
+            _lib.load_library(str(tmp_path / "nope.so"))
+    finally:
+        _lib._lib = saved
