@@ -1,0 +1,217 @@
+#!/usr/bin/env python3
+"""Throughput of the one-GPU Mega MoE forward on MI355X.
+
+One step = one moe_forward (dispatch -> Linear1 + SwiGLU + FP8 requant -> Linear2 +
+top-k weighting -> combine) over one batch of seeded synthetic inputs already resident in
+HBM; the weight transform (moe_prepare_weights) is done once beforehand, as the pages do
+it. Default workload: T=8192 tokens, E=8 experts, top-2, H=7168, I=18432 (the
+explainer's worked shape, chenxutan.com/d/1930 section 3.3).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c2]
+
+Prints one JSON line. FLOP = 6*T*k*H*I over valid slots only (2*P*H*2I for Linear1 plus
+2*P*I*H for Linear2). Stage times come from HIP events the library records on the
+launch stream between its kernels; the roofline object is for Linear1, the dominant
+kernel. The CPU baseline is the oracle (numpy fp64) timed on a bounded token sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused MoE FFN TFLOPS & % of MI355X FP8×FP4 MFMA peak; tokens/s (1 GPU)"
+PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA (FP8 x FP4 issues at the FP8 rate)
+PEAK_HBM_GBS = 8000.0
+GEMM_SRC = os.path.join(ROOT, "block_scaled_fp8_dispatch_amd", "csrc", "gemm.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="c2")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=4)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one plain device copy of this size first (for counter scaling)")
+    return ap.parse_args()
+
+
+def gemm_source_hash() -> str:
+    return hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()[:16]
+
+
+def load_traffic(cfg_name: str):
+    """HBM bytes per Linear1 launch from the committed counter summary, or None if the
+    kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"linear1_{cfg_name}_pmc.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"gemm_source_sha256_16:\s*([0-9a-f]+)", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != gemm_source_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+def cpu_baseline(inp_cpu: dict, cfg, n_tokens: int):
+    """Time the oracle on a few tokens whose top-k experts all lie in the two lowest expert
+    ids (so the sample decodes two experts' weights, not all of them)."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    idx = inp_cpu["topk_idx"]
+    pool = [t for t in range(idx.shape[0]) if np.all((idx[t] >= 0) & (idx[t] < 2))]
+    if len(pool) < n_tokens:
+        pool = list(range(idx.shape[0]))
+    toks = pool[:n_tokens]
+    t0 = time.perf_counter()
+    oracle.forward_inputs(inp_cpu, tokens=toks)
+    dt = time.perf_counter() - t0
+    slots = int(np.sum((idx[toks] >= 0) & (idx[toks] < cfg.E)))
+    flop = 6.0 * slots * cfg.H * cfg.I
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(toks)} tokens ({slots} slots, experts 0-1) of {cfg.name}, "
+                      f"{dt:.1f} s; numpy fp64, BLAS threads={threads}",
+            "seconds": dt}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); the multi-GPU "
+              "expert-parallel exchange is not part of it", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import block_scaled_fp8_dispatch_amd as moe
+    from synth import CONFIGS, make_inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    moe.load_library()
+    cfg = CONFIGS[args.config]
+    dev = "cuda"
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    inp = make_inputs(cfg, seed=args.seed, device=dev)
+    shape = moe.make_shape(cfg.E, cfg.H, cfg.I, cfg.k, cfg.T)
+    packed = torch.empty(moe.moe_packed_weights_bytes(shape), dtype=torch.uint8, device=dev)
+    moe.moe_prepare_weights(shape, inp.w1, inp.w1_sf, inp.w2, inp.w2_sf, packed)
+    ws = torch.empty(moe.moe_workspace_bytes(shape), dtype=torch.uint8, device=dev)
+    y = torch.empty(cfg.T, cfg.H, dtype=torch.int16, device=dev)
+    w1_bytes = inp.w1.numel() + inp.w1_sf.numel()
+    w2_bytes = inp.w2.numel() + inp.w2_sf.numel()
+    del inp.w1, inp.w1_sf, inp.w2, inp.w2_sf
+    torch.cuda.synchronize()
+
+    def step(events=None):
+        if events is None:
+            moe.moe_forward(y, inp.x_fp8, inp.x_sf, inp.topk_idx, inp.topk_weights, cfg.T, shape,
+                            packed, ws)
+        else:
+            moe.moe_forward_events(y, inp.x_fp8, inp.x_sf, inp.topk_idx, inp.topk_weights, cfg.T,
+                                   shape, packed, ws, events)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
+    for row in evs:          # create the HIP events before the timed region
+        for e in row:
+            e.record()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(K):
+        step(evs[i])
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(end)
+    ms = total_ms / K
+    stage = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(4)] for i in range(K)])
+    st_ms = stage.mean(axis=0)
+    yv = y.view(torch.bfloat16).float()
+    assert torch.isfinite(yv).all().item(), "non-finite output"
+
+    flop = cfg.flop
+    tflops = flop / (ms * 1e-3) / 1e12
+    P = cfg.T * cfg.k
+    l1_flop = 4.0 * P * cfg.H * cfg.I
+    l1_tflops = l1_flop / (st_ms[1] * 1e-3) / 1e12
+    traffic = load_traffic(cfg.name)
+    alg_bytes = (w1_bytes + w2_bytes + cfg.T * cfg.H + cfg.T * (4 * ((cfg.H + 511) // 512))
+                 + 8 * P + 2 * cfg.T * cfg.H)
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3 x fp4e2m1 -> f32 accumulate, bf16 out",
+        "data": "synthetic (seeded; x~N(0,1) FP8 1x128 UE8M0, W~N(0,0.02) FP4 1x32 UE8M0)",
+        "config": {"workload": f"{cfg.name}: T={cfg.T} E={cfg.E} top-{cfg.k} H={cfg.H} I={cfg.I} "
+                               f"{cfg.routing} routing", "T": cfg.T, "E": cfg.E, "k": cfg.k,
+                   "H": cfg.H, "I": cfg.I, "routing": cfg.routing, "parallelism": "single GPU"},
+        "tokens_per_s": round(cfg.T / (ms * 1e-3), 1),
+        "pct_fp8xfp4_peak": round(100 * tflops / PEAK_TFLOPS, 2),
+        "alg_hbm_gbs": round(alg_bytes / (ms * 1e-3) / 1e9, 1),
+        "stage_ms": {"dispatch": round(float(st_ms[0]), 4), "linear1": round(float(st_ms[1]), 4),
+                     "linear2": round(float(st_ms[2]), 4), "combine": round(float(st_ms[3]), 4)},
+        "wall_s_timed": round(wall, 3),
+        "roofline": {"bound": "mfma", "kernel": "Linear1 grouped GEMM (+SwiGLU/requant epilogue)",
+                     "achieved": round(l1_tflops, 2), "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(l1_tflops / PEAK_TFLOPS, 4), "traffic": traffic},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print(f"[bench] timing the CPU oracle on {args.cpu_sample_tokens} tokens ...", file=sys.stderr,
+              flush=True)
+        idx = inp.topk_idx.cpu().numpy()
+        # host copies of what the sample needs: its tokens and the two experts' weights
+        from synth import make_weights
+        w1, w1_sf, w2, w2_sf = make_weights(cfg, seed=args.seed, device=dev)
+        host = {"x_fp8": inp.x_fp8.cpu().numpy(), "x_sf": inp.x_sf.cpu().numpy(),
+                "topk_idx": idx, "topk_weights": inp.topk_weights.cpu().numpy(),
+                "w1": w1.cpu().numpy(), "w1_sf": w1_sf.cpu().numpy(),
+                "w2": w2.cpu().numpy(), "w2_sf": w2_sf.cpu().numpy()}
+        del w1, w1_sf, w2, w2_sf
+        cb = cpu_baseline(host, cfg, args.cpu_sample_tokens)
+        cb.pop("seconds")
+        out["cpu_baseline"] = cb
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -6,7 +6,7 @@ not load the library; the first call does, and raises if it has not been built.
 """
 from ._lib import (EXPORTED, LIB_PATH, MOE_ERR_ALIGN, MOE_ERR_HIP, MOE_ERR_NULL, MOE_ERR_SHAPE,
                    MOE_ERR_TOKENS, MOE_ERR_WORKSPACE, MOE_OK, MoEError, load_library, make_shape,
-                   moe_forward, moe_forward_raw, moe_layout_t, moe_packed_weights_bytes,
+                   moe_forward, moe_forward_events, moe_forward_raw, moe_layout_t, moe_packed_weights_bytes,
                    moe_prepare_weights, moe_prepare_weights_raw, moe_read_diagnostics,
                    moe_shape_t, moe_status_string, moe_version, moe_workspace_bytes,
                    moe_workspace_layout)
@@ -14,6 +14,6 @@ from ._lib import (EXPORTED, LIB_PATH, MOE_ERR_ALIGN, MOE_ERR_HIP, MOE_ERR_NULL,
 __all__ = ["EXPORTED", "LIB_PATH", "MOE_OK", "MOE_ERR_NULL", "MOE_ERR_SHAPE", "MOE_ERR_ALIGN",
            "MOE_ERR_WORKSPACE", "MOE_ERR_TOKENS", "MOE_ERR_HIP", "MoEError", "load_library",
            "make_shape", "moe_shape_t", "moe_layout_t", "moe_packed_weights_bytes",
-           "moe_prepare_weights", "moe_prepare_weights_raw", "moe_workspace_bytes", "moe_forward",
+           "moe_prepare_weights", "moe_prepare_weights_raw", "moe_workspace_bytes", "moe_forward", "moe_forward_events",
            "moe_forward_raw", "moe_workspace_layout", "moe_read_diagnostics", "moe_status_string",
            "moe_version"]

@@ -22,7 +22,7 @@ MOE_ERR_TOKENS = -5
 MOE_ERR_HIP = -6
 
 EXPORTED = ("moe_packed_weights_bytes", "moe_prepare_weights", "moe_workspace_bytes",
-            "moe_forward", "moe_workspace_layout", "moe_read_diagnostics",
+            "moe_forward", "moe_forward_events", "moe_workspace_layout", "moe_read_diagnostics",
             "moe_status_string", "moe_version")
 
 
@@ -70,6 +70,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_workspace_bytes.restype = S
     lib.moe_forward.argtypes = [P, P, P, P, P, I32, shp, P, P, S, P]
     lib.moe_forward.restype = ctypes.c_int
+    lib.moe_forward_events.argtypes = [P, P, P, P, P, I32, shp, P, P, S, P, ctypes.POINTER(P)]
+    lib.moe_forward_events.restype = ctypes.c_int
     lib.moe_workspace_layout.argtypes = [shp, I32, ctypes.POINTER(moe_layout_t)]
     lib.moe_workspace_layout.restype = ctypes.c_int
     lib.moe_read_diagnostics.argtypes = [shp, P, ctypes.POINTER(I32), ctypes.POINTER(I32), P]
@@ -139,6 +141,30 @@ def moe_forward(y, x_fp8, x_sf, topk_idx, topk_weights, num_tokens: int, shape: 
         ctypes.byref(shape), _ptr(packed), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "moe_forward")
+
+
+def moe_forward_events(y, x_fp8, x_sf, topk_idx, topk_weights, num_tokens: int,
+                       shape: moe_shape_t, packed, workspace, events, stream=None) -> None:
+    """moe_forward that also records 5 torch.cuda.Event objects at the stage boundaries
+    (before dispatch, after dispatch, after Linear1, after Linear2, after the combine)."""
+    handles = (ctypes.c_void_p * 5)(*[_event_handle(e) for e in events])
+    st = load_library().moe_forward_events(
+        _ptr(y), _ptr(x_fp8), _ptr(x_sf), _ptr(topk_idx), _ptr(topk_weights), int(num_tokens),
+        ctypes.byref(shape), _ptr(packed), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream), handles)
+    _check(st, "moe_forward_events")
+
+
+def _event_handle(ev) -> int:
+    if isinstance(ev, int):
+        return ev
+    h = ev.cuda_event
+    if not h:
+        # torch creates the HIP event lazily, on its first record
+        import torch
+        ev.record(torch.cuda.current_stream())
+        h = ev.cuda_event
+    return h
 
 
 def moe_forward_raw(y_ptr, x_ptr, xsf_ptr, idx_ptr, w_ptr, num_tokens, shape, packed_ptr,

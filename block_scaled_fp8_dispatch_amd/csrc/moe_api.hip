@@ -133,10 +133,10 @@ int moe_prepare_weights(const moe_shape_t* shape, const uint8_t* w1, const uint8
     return MOE_OK;
 }
 
-int moe_forward(uint16_t* y_bf16, const uint8_t* x_fp8, const uint8_t* x_sf,
-                const int32_t* topk_idx, const float* topk_weights, int32_t num_tokens,
-                const moe_shape_t* shape, const void* packed, void* workspace,
-                size_t workspace_bytes, hipStream_t stream) {
+static int forward_impl(uint16_t* y_bf16, const uint8_t* x_fp8, const uint8_t* x_sf,
+                        const int32_t* topk_idx, const float* topk_weights, int32_t num_tokens,
+                        const moe_shape_t* shape, const void* packed, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream, hipEvent_t* events) {
     if (!shape) return MOE_ERR_NULL;
     if (!shape_ok(shape)) return MOE_ERR_SHAPE;
     if (num_tokens < 0 || num_tokens > shape->max_tokens) return MOE_ERR_TOKENS;
@@ -148,6 +148,7 @@ int moe_forward(uint16_t* y_bf16, const uint8_t* x_fp8, const uint8_t* x_sf,
     const WsLayout W = ws_layout(*shape);
     if (workspace_bytes < W.pub.total) return MOE_ERR_WORKSPACE;
     if (num_tokens == 0) return MOE_OK;
+    auto mark = [&](int i) { return events ? hipEventRecord(events[i], stream) : hipSuccess; };
 
     const moe_shape_t& s = *shape;
     const int T = num_tokens, E = s.num_experts, H = s.hidden, I = s.intermediate, k = s.num_topk;
@@ -159,10 +160,12 @@ int moe_forward(uint16_t* y_bf16, const uint8_t* x_fp8, const uint8_t* x_sf,
     int32_t* tile_e = i32(W.pub.tile_expert);
     int32_t* tile_r = i32(W.pub.tile_row0);
 
+    if (mark(0) != hipSuccess) return MOE_ERR_HIP;
     if (launch_route(topk_idx, T * k, E, BM, i32(W.blk), meta, i32(W.pub.counts),
                      i32(W.pub.offsets), perm, i32(W.pub.inv), tile_e, tile_r, W.pub.max_tiles,
                      stream) != hipSuccess)
         return MOE_ERR_HIP;
+    if (mark(1) != hipSuccess) return MOE_ERR_HIP;
 
     const PackedLayout L = packed_layout(s);
     const uint8_t* pk = static_cast<const uint8_t*>(packed);
@@ -194,6 +197,7 @@ int moe_forward(uint16_t* y_bf16, const uint8_t* x_fp8, const uint8_t* x_sf,
     a1.h_stride = I;
     a1.h_sf_stride = (int)W.pub.h_sf_stride;
     if (launch_linear1(BM, a1, stream) != hipSuccess) return MOE_ERR_HIP;
+    if (mark(2) != hipSuccess) return MOE_ERR_HIP;
 
     GemmArgs a2 = a1;
     a2.a = ws + W.pub.h8;
@@ -212,11 +216,32 @@ int moe_forward(uint16_t* y_bf16, const uint8_t* x_fp8, const uint8_t* x_sf,
     a2.topk_weights = topk_weights;
     a2.out_cols = H;
     if (launch_linear2(BM, a2, stream) != hipSuccess) return MOE_ERR_HIP;
+    if (mark(3) != hipSuccess) return MOE_ERR_HIP;
 
     if (launch_combine(reinterpret_cast<const uint16_t*>(ws + W.pub.stage), topk_idx, T, k, E, H,
                        y_bf16, stream) != hipSuccess)
         return MOE_ERR_HIP;
+    if (mark(4) != hipSuccess) return MOE_ERR_HIP;
     return MOE_OK;
+}
+
+int moe_forward(uint16_t* y_bf16, const uint8_t* x_fp8, const uint8_t* x_sf,
+                const int32_t* topk_idx, const float* topk_weights, int32_t num_tokens,
+                const moe_shape_t* shape, const void* packed, void* workspace,
+                size_t workspace_bytes, hipStream_t stream) {
+    return forward_impl(y_bf16, x_fp8, x_sf, topk_idx, topk_weights, num_tokens, shape, packed,
+                        workspace, workspace_bytes, stream, nullptr);
+}
+
+int moe_forward_events(uint16_t* y_bf16, const uint8_t* x_fp8, const uint8_t* x_sf,
+                       const int32_t* topk_idx, const float* topk_weights, int32_t num_tokens,
+                       const moe_shape_t* shape, const void* packed, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream, hipEvent_t* events) {
+    if (!events) return MOE_ERR_NULL;
+    for (int i = 0; i < 5; ++i)
+        if (!events[i]) return MOE_ERR_NULL;
+    return forward_impl(y_bf16, x_fp8, x_sf, topk_idx, topk_weights, num_tokens, shape, packed,
+                        workspace, workspace_bytes, stream, events);
 }
 
 int moe_read_diagnostics(const moe_shape_t* shape, const void* workspace, int32_t* invalid_ids,

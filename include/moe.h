@@ -109,6 +109,18 @@ int moe_forward(uint16_t* y_bf16,
                 int32_t num_tokens, const moe_shape_t* shape, const void* packed,
                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* moe_forward, also recording five caller-created events on `stream` at the stage
+ * boundaries: events[0] before dispatch, [1] after dispatch, [2] after Linear1 (with its
+ * SwiGLU/requant epilogue), [3] after Linear2 (with its weighting epilogue), [4] after
+ * the combine. For per-stage timing with hipEventElapsedTime; nothing synchronises.
+ * events must point to 5 valid hipEvent_t; other arguments as for moe_forward. */
+int moe_forward_events(uint16_t* y_bf16,
+                       const uint8_t* x_fp8, const uint8_t* x_sf,
+                       const int32_t* topk_idx, const float* topk_weights,
+                       int32_t num_tokens, const moe_shape_t* shape, const void* packed,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream,
+                       hipEvent_t* events);
+
 /* Where the last moe_forward on `workspace` left its routing tables and
  * intermediates (byte offsets from the workspace base; for tests and tools). */
 typedef struct {

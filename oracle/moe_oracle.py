@@ -122,16 +122,28 @@ def unpack_e2m1(packed: np.ndarray) -> np.ndarray:
 
 def dequant_fp8_rows(codes: np.ndarray, sf: np.ndarray, K: int) -> np.ndarray:
     """x[r, c] = e4m3(codes[r, c]) * 2^(sf[r, c // 128] - 127)  [P1 11.1; per 1x128]."""
-    vals = decode_e4m3(codes[:, :K])
+    R = codes.shape[0]
+    vals = decode_e4m3(codes[:, :K]).reshape(R, K // 128, 128)
     scale = decode_ue8m0(sf[:, : K // 128])
-    return vals * np.repeat(scale, 128, axis=1)
+    return (vals * scale[:, :, None]).reshape(R, K)
 
 
-def dequant_fp4_rows(packed: np.ndarray, sf: np.ndarray, K: int) -> np.ndarray:
-    """w[n, c] = e2m1(nibble(n, c)) * 2^(sf[n, c // 32] - 127)  [P1 11.1; per 1x32]."""
-    vals = E2M1_TABLE[unpack_e2m1(packed)[:, :K]]
+# value pair of each packed byte: (element 2i = low nibble, element 2i+1 = high nibble)
+_E2M1_PAIRS = np.stack([E2M1_TABLE[np.arange(256) & 0x0F], E2M1_TABLE[np.arange(256) >> 4]], axis=1)
+
+
+def dequant_fp4_rows(packed: np.ndarray, sf: np.ndarray, K: int, out=None) -> np.ndarray:
+    """w[n, c] = e2m1(nibble(n, c)) * 2^(sf[n, c // 32] - 127)  [P1 11.1; per 1x32].
+    `out` (optional, f64 [R, K]) is filled and returned."""
+    R = packed.shape[0]
+    if out is None:
+        out = np.empty((R, K), dtype=np.float64)
+    np.take(_E2M1_PAIRS, np.asarray(packed, dtype=np.uint8)[:, : K // 2], axis=0,
+            out=out.reshape(R, K // 2, 2))
     scale = decode_ue8m0(sf[:, : K // 32])
-    return vals * np.repeat(scale, 32, axis=1)
+    v = out.reshape(R, K // 32, 32)
+    np.multiply(v, scale[:, :, None], out=v)
+    return out
 
 
 # ----------------------------------------------------------------------------
@@ -270,21 +282,20 @@ def route(topk_idx: np.ndarray, E: int, BM: int) -> Dict[str, np.ndarray]:
 # ----------------------------------------------------------------------------
 
 
-def linear1(xr: np.ndarray, w1e: np.ndarray, w1e_sf: np.ndarray, row_chunk: int = 4096):
+def linear1(xr: np.ndarray, w1e: np.ndarray, w1e_sf: np.ndarray, row_chunk: int = 1024):
     """G = xr . W1_gate^T, U = xr . W1_up^T for one expert, fp64 [P1 3.1 step 2; 4.2].
     xr: dequantised activation rows [R, H]; w1e u8 [2I, H/2]; w1e_sf u8 [2I, H/32]."""
     R, H = xr.shape
     I = w1e.shape[0] // 2
     G = np.empty((R, I))
     U = np.empty((R, I))
-    for r0 in range(0, I, row_chunk):                                     # bound memory
+    buf = np.empty((min(row_chunk, I), H))                                # reused: bounds memory
+    for r0 in range(0, I, row_chunk):
         r1 = min(I, r0 + row_chunk)
-        Wg = dequant_fp4_rows(w1e[r0:r1], w1e_sf[r0:r1], H)
+        Wg = dequant_fp4_rows(w1e[r0:r1], w1e_sf[r0:r1], H, out=buf[: r1 - r0])
         G[:, r0:r1] = xr @ Wg.T
-        del Wg
-        Wu = dequant_fp4_rows(w1e[I + r0:I + r1], w1e_sf[I + r0:I + r1], H)
+        Wu = dequant_fp4_rows(w1e[I + r0:I + r1], w1e_sf[I + r0:I + r1], H, out=buf[: r1 - r0])
         U[:, r0:r1] = xr @ Wu.T
-        del Wu
     return G, U
 
 
@@ -296,7 +307,7 @@ def swiglu(g: np.ndarray, u: np.ndarray) -> np.ndarray:
 
 def forward(x_fp8, x_sf, topk_idx, topk_weights, w1, w1_sf, w2, w2_sf,
             tokens: Optional[Sequence[int]] = None, cols: Optional[Sequence[int]] = None,
-            row_chunk: int = 4096, keep_intermediates: bool = True):
+            row_chunk: int = 1024, keep_intermediates: bool = True):
     """The Mega MoE forward of one device's local experts [P1 3.1-3.3; P2 5].
 
     Shapes: x_fp8 u8 [T,H]; x_sf u8 [T, >=H/128]; topk_idx i32 [T,k]; topk_weights
@@ -338,8 +349,12 @@ def forward(x_fp8, x_sf, topk_idx, topk_weights, w1, w1_sf, w2, w2_sf,
         G, U = linear1(xr, w1[e], w1_sf[e], row_chunk)
         h = swiglu(G, U)
         q, sf, hd = requant_fp8_1x128(h)
-        W2c = dequant_fp4_rows(w2[e][cols_arr], w2_sf[e][cols_arr], I)   # [len(cols), I]
-        O = hd @ W2c.T                                                    # [R, len(cols)]
+        O = np.empty((len(slots), len(cols_arr)))                          # [R, len(cols)]
+        buf = np.empty((min(row_chunk, len(cols_arr)), I))
+        for c0 in range(0, len(cols_arr), row_chunk):
+            cc = cols_arr[c0:c0 + row_chunk]
+            W2c = dequant_fp4_rows(w2[e][cc], w2_sf[e][cc], I, out=buf[: len(cc)])
+            O[:, c0:c0 + len(cc)] = hd @ W2c.T
         for r, (t, j) in enumerate(slots):
             contrib[tok_pos[t], j] = float(topk_weights[t, j]) * O[r]
             if keep_intermediates:
