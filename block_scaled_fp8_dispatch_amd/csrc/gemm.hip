@@ -10,13 +10,19 @@
 //     top-k weight and writes it, as bf16, to the staging row of its (token, slot) (the
 //     combine of step 5 then sums a token's slots in slot order, without atomics).
 //
-// Tiling. A workgroup of 4 waves owns one BM x 256 output tile of one expert's rows
-// (row tiles come from the dispatch tile list; an expert's group is padded to BM rows).
-// Each K step (128) stages the A tile (BM x 128 bytes, XOR-swizzled 16-byte chunks) and
-// the B tile (16 packed fragments, 16 KB) in LDS, double-buffered with one barrier per
-// step; the next step's global loads are in flight while the MFMAs of this step run.
-// Scales are read straight from global memory: one 32-bit word per lane covers four K
-// steps, and the instruction's byte select picks the step.
+// Tiling. A workgroup of 4 waves owns a BM x 256 output tile of one expert's rows (row
+// tiles come from the dispatch tile list; an expert's group is padded to BM rows).
+//
+// Pipeline. The A tile of a K step (BM x 128 bytes, XOR-swizzled 16-byte chunks) and the
+// B tile (16 packed fragments, 16 KB) are fetched straight into a 3-slot LDS ring with
+// gfx950's global_load_lds_dwordx4 (no staging registers). There is one barrier per K
+// step, half way through its MFMAs: after it the loads two steps ahead are issued and the
+// next step's B fragments and first A fragment are read into registers, so MFMAs never
+// wait on LDS at a step boundary and every tile load has a full step to arrive. The steps
+// are branch-free and carry scheduling-group hints, so the compiler places one load
+// between consecutive MFMAs instead of issuing the loads as a burst. Scales are read
+// straight from global memory: one 32-bit word per lane covers four K steps, and the
+// instruction's byte select picks the step.
 //
 // Operand layout of the 16x16x128 instruction with A = FP8, B = FP4 (measured on gfx950):
 //   A lane 16g+i : row i, bytes 0..15 = K[16g, 16g+16), bytes 16..31 = K[64+16g, 64+16g+16)
@@ -24,9 +30,10 @@
 //   scale lane 16b+i (A) / 16b+j (B): the 32-block b of row i / column j
 //   C lane l     : C[4*(l/16) + r][l%16], r = 0..3
 //
-// Launch mapping. Workgroups go round-robin to the 8 XCDs (id mod 8). Each XCD gets a
-// contiguous range of tile ids, and tile ids walk groups of 4 row tiles across all column
-// tiles, so the workgroups resident on one XCD share A rows and B columns in its L2.
+// Launch mapping. Workgroups go round-robin to the 8 XCDs (id mod 8). Each XCD owns a
+// contiguous range of tile ids and its workgroups take consecutive ids in each round;
+// tile ids walk groups of 4 row tiles across all column tiles, so the tiles resident on
+// one XCD at any time share A rows and B columns in its L2.
 #include "moe_internal.h"
 
 namespace moe {
@@ -36,13 +43,30 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
 constexpr int kGroupM = 4;
+constexpr int kThreads = 256;
+constexpr int kStages = 3;
+// Word 3 of a raw buffer descriptor on gfx950 (32-bit data format, no swizzle); with a zero
+// stride and a record count of 2^31-1 bytes, offsets are plain byte offsets.
+constexpr int kRsrcWord3 = 0x00020000;
 
 template <int N>
 struct IntC {
     static constexpr int value = N;
 };
+
+#define MOE_GPTR(p) ((__attribute__((address_space(1))) void*)(p))
+#define MOE_LPTR(p) ((__attribute__((address_space(3))) void*)(p))
+
+// Wait for this wave's outstanding vector-memory operations (the direct-to-LDS tile loads
+// included), then meet the other waves. One asm statement with a memory clobber, so no
+// LDS access is moved across it.
+__device__ inline void wait_vmem_barrier() { asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory"); }
+// Wait for this wave's LDS accesses, then meet the other waves.
+__device__ inline void wait_lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// Meet the other waves (every LDS value this wave read has already been consumed).
+__device__ inline void plain_barrier() { asm volatile("s_barrier" ::: "memory"); }
+__device__ inline void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 __device__ inline uint16_t f32_to_bf16_rne(float v) {
     uint32_t b = __float_as_uint(v);
@@ -63,34 +87,56 @@ __device__ inline int requant_scale_byte(float amax) {
     return b < 0 ? 0 : b;
 }
 
+// silu(g) * u = g * u / (1 + e^-g), with the hardware exp2 and reciprocal (about 1 ulp each)
+__device__ inline float swiglu(float g, float u) {
+    const float e = __builtin_amdgcn_exp2f(-g * 1.4426950408889634f);
+    return g * u * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+template <int BM, int WAVES_M, int WAVES_N, int MODE>
+struct Cfg {
+    static constexpr int WM = BM / WAVES_M;
+    static constexpr int WN = kBN / WAVES_N;
+    static constexpr int FM = WM / 16;
+    static constexpr int FN = WN / 16;
+    static constexpr int A_BYTES = BM * kBK;
+    static constexpr int STAGE_BYTES = A_BYTES + kBTileBytes;
+    static constexpr int A_DMA = A_BYTES / 1024 / 4;   // 1 KB direct-to-LDS loads per wave
+    static constexpr int B_DMA = kBTileBytes / 1024 / 4;
+    static constexpr int DMA = A_DMA + B_DMA;
+    static_assert(WAVES_M * WAVES_N == 4, "4 waves");
+    static_assert(FM >= 2 && FM % 2 == 0, "mid-step split");
+    static_assert(MODE != 1 || WAVES_N * (FN / 2) == 8, "gate/up pairing");
+    static_assert(MODE != 1 || BM * 128 + 4 * WAVES_N * BM <= STAGE_BYTES, "epilogue fits a slot");
+    static_assert(MODE != 2 || 4 * 16 * WN * 2 <= STAGE_BYTES, "epilogue fits a slot");
+};
+
 template <int BM, int WAVES_M, int WAVES_N, int MODE>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args) {
-    constexpr int WM = BM / WAVES_M;
-    constexpr int WN = kBN / WAVES_N;
-    constexpr int FM = WM / 16;
-    constexpr int FN = WN / 16;
-    constexpr int A_BYTES = BM * kBK;                 // fp8: one byte per element
-    constexpr int STAGE_BYTES = A_BYTES + kBTileBytes;
-    constexpr int A_ROWS_PER_THREAD = BM / 32;        // 8 threads x 16 B per 128-byte row
-    static_assert(WAVES_M * WAVES_N == 4, "4 waves");
-    static_assert(MODE != 1 || WAVES_N * (FN / 2) == 8, "gate/up pairing");
+    // The body uses gfx950 buffer descriptors, a device-only type: the host pass of the
+    // split compilation sees an empty kernel and emits only its launch stub.
+#if defined(__HIP_DEVICE_COMPILE__)
+    using C = Cfg<BM, WAVES_M, WAVES_N, MODE>;
+    constexpr int WM = C::WM, WN = C::WN, FM = C::FM, FN = C::FN;
+    constexpr int A_BYTES = C::A_BYTES, STAGE_BYTES = C::STAGE_BYTES;
+    constexpr int A_DMA = C::A_DMA, B_DMA = C::B_DMA, DMA = C::DMA;
 
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * STAGE_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WAVES_N;
     const int wn = wave % WAVES_N;
+    const int g = lane >> 4;
 
-    // ---- tile id -> (row tile, column tile), XCD-aware --------------------------------
+    // ---- tile id -> (row tile, column tile), XCD-aware ----------------------------------
     int num_mt = args.meta[0];
     if (num_mt > args.max_tiles) num_mt = args.max_tiles;
     const int NT = args.n_tiles;
     const int total = num_mt * NT;
-    const int bid = blockIdx.x;
-    const int xcd = bid & 7;
-    const int li = bid >> 3;
+    const int xcd = blockIdx.x & 7;
+    const int li = blockIdx.x >> 3;
     const int per = total >> 3, rem = total & 7;
     if (li >= per + (xcd < rem ? 1 : 0)) return;
     const int v = xcd * per + (xcd < rem ? xcd : rem) + li;
@@ -102,231 +148,285 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
     const int nt = vin / gm;
     const int expert = args.tile_expert[mt];
     const int row0 = args.tile_row0[mt];
+    const int nks = args.K / kBK;              // >= 2
 
-    const int K = args.K;
-    const int nks = K / kBK;
-    const int nkb = (nks + 3) / 4;
-
-    // ---- A row sources (staging) and A scale sources (per lane) ------------------------
-    const int chunk = tid & 7;
-    uint32_t a_off[A_ROWS_PER_THREAD];
+    // ---- A rows this lane fetches and reads scales for ----------------------------------
+    // Every tile load and scale load is a buffer load: 32-bit per-lane offset in a VGPR,
+    // per-step offset in an SGPR, base in a descriptor. DMA j of wave w fills LDS rows
+    // 8*(w*A_DMA + j) .. +7 of the A tile; lane l lands at row + l/8, physical 16-byte chunk
+    // l%8, which holds logical chunk (l%8) ^ (row%8).
+    const int a_chunk = (lane & 7) ^ (lane >> 3);
+    uint32_t a_off[A_DMA];
 #pragma unroll
-    for (int i = 0; i < A_ROWS_PER_THREAD; ++i) {
-        const int r = (tid >> 3) + 32 * i;
+    for (int j = 0; j < A_DMA; ++j) {
+        const int r = 8 * (wave * A_DMA + j) + (lane >> 3);
+        uint32_t row;
         if (MODE == 1) {
             const int slot = args.perm[row0 + r];
-            const int tok = slot >= 0 ? slot / args.topk : 0;
-            a_off[i] = (uint32_t)tok * (uint32_t)args.a_stride;
+            row = slot >= 0 ? (uint32_t)(slot / args.topk) : 0u;
         } else {
-            a_off[i] = (uint32_t)(row0 + r) * (uint32_t)args.a_stride;
+            row = (uint32_t)(row0 + r);
         }
+        a_off[j] = row * (uint32_t)args.a_stride + a_chunk * 16;
     }
     uint32_t sa_off[FM];
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
         const int r = wm * WM + fm * 16 + (lane & 15);
+        uint32_t row;
         if (MODE == 1) {
             const int slot = args.perm[row0 + r];
-            const int tok = slot >= 0 ? slot / args.topk : 0;
-            sa_off[fm] = (uint32_t)tok * (uint32_t)args.a_sf_stride;
+            row = slot >= 0 ? (uint32_t)(slot / args.topk) : 0u;
         } else {
-            sa_off[fm] = (uint32_t)(row0 + r) * (uint32_t)args.a_sf_stride;
+            row = (uint32_t)(row0 + r);
         }
+        sa_off[fm] = row * (uint32_t)args.a_sf_stride;
     }
     // B fragment index of the wave's n-th fragment
     auto bfrag = [&](int fn) __attribute__((always_inline)) -> int {
         if (MODE == 1) return fn < FN / 2 ? wn * (FN / 2) + fn : 8 + wn * (FN / 2) + (fn - FN / 2);
         return wn * FN + fn;
     };
-    const uint8_t* bdata = args.b + (size_t)expert * args.b_expert + (size_t)nt * args.b_ntile;
-    const uint32_t* bscale = args.b_sf + (size_t)expert * args.bs_expert + (size_t)nt * args.bs_ntile;
+    const __amdgpu_buffer_rsrc_t rs_a = __builtin_amdgcn_make_buffer_rsrc((void*)args.a, 0, 0x7fffffff, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rs_asf = __builtin_amdgcn_make_buffer_rsrc((void*)args.a_sf, 0, 0x7fffffff, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rs_b = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(args.b + (size_t)expert * args.b_expert + (size_t)nt * args.b_ntile), 0, 0x7fffffff, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rs_bsf = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(args.b_sf + (size_t)expert * args.bs_expert + (size_t)nt * args.bs_ntile), 0, 0x7fffffff, kRsrcWord3);
+    const uint32_t b_voff = (uint32_t)(wave * B_DMA * 1024 + lane * 16);
+    const uint32_t bs_voff = (uint32_t)(lane * 4);
+
+    // one direct-to-LDS load (j < A_DMA: A rows, else B fragments) of K step ks into ring
+    // slot `slot` (ks is clamped by the caller)
+    auto dma_one = [&](int ks, int slot, int j) __attribute__((always_inline)) {
+        uint8_t* As = smem + slot * STAGE_BYTES;
+        if (j < A_DMA) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_a, MOE_LPTR(As + (wave * A_DMA + j) * 1024), 16,
+                                                     a_off[j], ks * kBK, 0, 0);
+        } else {
+            const int jj = j - A_DMA;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_b, MOE_LPTR(As + A_BYTES + (wave * B_DMA + jj) * 1024),
+                                                     16, b_voff, ks * kBTileBytes + jj * 1024, 0, 0);
+        }
+    };
+    // one scale word (i < FM: A row block, else B fragment) of the 4-step block holding ks
+    auto scale_one = [&](int ks, int i, uint32_t* sa, uint32_t* sb) __attribute__((always_inline)) {
+        const int kb = ks >> 2;
+        if (i < FM) sa[i] = __builtin_amdgcn_raw_buffer_load_b32(rs_asf, sa_off[i], 4 * kb, 0);
+        else sb[i - FM] = __builtin_amdgcn_raw_buffer_load_b32(rs_bsf, bs_voff + bfrag(i - FM) * 256,
+                                                               kb * kBScaleBlockBytes, 0);
+    };
+    // LDS fragment reads: per-lane base addresses; fragment and slot offsets are uniform
+    const uint32_t a_lo = (uint32_t)((wm * WM + (lane & 15)) * kBK + ((g ^ (lane & 7)) << 4));
+    const uint32_t a_hi = (uint32_t)((wm * WM + (lane & 15)) * kBK + (((g + 4) ^ (lane & 7)) << 4));
+    const uint32_t b_rd = (uint32_t)(A_BYTES + lane * 16);
+    auto read_a = [&](int slot, int fm) __attribute__((always_inline)) -> v8i {
+        const uint8_t* As = smem + slot * STAGE_BYTES + fm * 16 * kBK;
+        const v4i lo4 = *reinterpret_cast<const v4i*>(As + a_lo);
+        const v4i hi4 = *reinterpret_cast<const v4i*>(As + a_hi);
+        return (v8i){lo4.x, lo4.y, lo4.z, lo4.w, hi4.x, hi4.y, hi4.z, hi4.w};
+    };
+    auto read_b = [&](int slot, int fn) __attribute__((always_inline)) -> v4i {
+        const uint8_t* Bs = smem + slot * STAGE_BYTES + bfrag(fn) * kFragBytes;
+        return *reinterpret_cast<const v4i*>(Bs + b_rd);
+    };
 
     v4f acc[FM][FN];
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = (v4f){0.f, 0.f, 0.f, 0.f};
+    v4i bq[FN];
+    v8i a_cur, a_nx;
+    uint32_t sa_cur[FM], sb_cur[FN], sa_nx[FM], sb_nx[FN];
 
-    v4i a_st[A_ROWS_PER_THREAD];
-    v4i b_st[4];
-    auto load_stage = [&](int ks) __attribute__((always_inline)) {
+    // prologue: K steps 0 and 1
 #pragma unroll
-        for (int i = 0; i < A_ROWS_PER_THREAD; ++i)
-            a_st[i] = *reinterpret_cast<const v4i*>(args.a + a_off[i] + (size_t)ks * kBK + chunk * 16);
-        const uint8_t* bsrc = bdata + (size_t)ks * kBTileBytes;
+    for (int j = 0; j < DMA; ++j) dma_one(0, 0, j);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            b_st[i] = *reinterpret_cast<const v4i*>(bsrc + (tid + kThreads * i) * 16);
-    };
-    auto store_stage = [&](int buf) __attribute__((always_inline)) {
-        uint8_t* As = smem + buf * STAGE_BYTES;
-        uint8_t* Bs = As + A_BYTES;
+    for (int j = 0; j < DMA; ++j) dma_one(1, 1, j);
 #pragma unroll
-        for (int i = 0; i < A_ROWS_PER_THREAD; ++i) {
-            const int r = (tid >> 3) + 32 * i;
-            *reinterpret_cast<v4i*>(As + r * kBK + ((chunk ^ (r & 7)) << 4)) = a_st[i];
-        }
+    for (int i = 0; i < FM + FN; ++i) scale_one(0, i, sa_cur, sb_cur);
+    wait_vmem_barrier();
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            *reinterpret_cast<v4i*>(Bs + (tid + kThreads * i) * 16) = b_st[i];
-    };
+    for (int fn = 0; fn < FN; ++fn) bq[fn] = read_b(0, fn);
+    a_nx = read_a(0, 0);
 
-    uint32_t sa_cur[FM], sb_cur[FN], sa_nxt[FM], sb_nxt[FN];
-    auto load_scales = [&](int kb, uint32_t* sa, uint32_t* sb) __attribute__((always_inline)) {
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm)
-            sa[fm] = *reinterpret_cast<const uint32_t*>(args.a_sf + sa_off[fm] + 4 * kb);
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn)
-            sb[fn] = bscale[(size_t)kb * (16 * 64) + bfrag(fn) * 64 + lane];
-    };
-
-    const int g = lane >> 4;
-    const int sw = lane & 7;   // row & 7 for every row this lane reads
-    auto compute = [&](int buf, auto ops_c) __attribute__((always_inline)) {
+    // One K step, free of branches and scheduled by hand: every MFMA is followed by at most
+    // a few memory operations, in a fixed order the compiler may not change (scheduling
+    // barriers that only let ALU work move). Each A fragment is read right after the first
+    // MFMA of the fragment before it. Half way: barrier (this wave's loads of step ks+1 have
+    // landed, every wave is past step ks-1); in the second half, the loads of step ks+2
+    // (clamped to the last step: a harmless reload into a free slot) and, in the third step
+    // of each 4-step block, the scale words of the next block (needed only after the next
+    // barrier, which waits for them) go one or a few per MFMA. The last A fragment's MFMAs
+    // reload each B fragment register with the next step's fragment right after its last
+    // use, and the next step's first A fragment is read with them: no double buffers.
+    auto step = [&](int ks, auto ops_c) __attribute__((always_inline)) {
         constexpr int OPS = decltype(ops_c)::value;
-        const uint8_t* As = smem + buf * STAGE_BYTES;
-        const uint8_t* Bs = As + A_BYTES;
-        v4i bq[FN];
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn)
-            bq[fn] = *reinterpret_cast<const v4i*>(Bs + bfrag(fn) * kFragBytes + lane * 16);
+        constexpr int HALF = FM / 2 * FN;
+        constexpr int NOPS = DMA + (OPS == 2 ? FM + FN : 0);
+        constexpr int PER = (NOPS + HALF - 1) / HALF;
+        const int slot = ks % kStages;
+        const int slot1 = (ks + 1) % kStages;
+        const int slot2 = (ks + 2) % kStages;
+        const int ks2 = min(ks + 2, nks - 1);
+        auto issue = [&](int op) __attribute__((always_inline)) {
+            if (op < DMA) dma_one(ks2, slot2, op);
+            else if (op < NOPS) scale_one(ks2, op - DMA, sa_nx, sb_nx);
+        };
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) {
-            const int r = wm * WM + fm * 16 + (lane & 15);
-            const v4i lo = *reinterpret_cast<const v4i*>(As + r * kBK + ((g ^ sw) << 4));
-            const v4i hi = *reinterpret_cast<const v4i*>(As + r * kBK + (((g + 4) ^ sw) << 4));
-            const v8i a = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            a_cur = a_nx;
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn) {
                 const v8i b = {bq[fn].x, bq[fn].y, bq[fn].z, bq[fn].w, 0, 0, 0, 0};
                 acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    a, b, acc[fm][fn], 0, 4, OPS, (int)sa_cur[fm], OPS, (int)sb_cur[fn]);
+                    a_cur, b, acc[fm][fn], 0, 4, OPS, (int)sa_cur[fm], OPS, (int)sb_cur[fn]);
+                if (fn == 0) a_nx = fm + 1 < FM ? read_a(slot, fm + 1) : read_a(slot1, 0);
+                if (fm == FM - 1) bq[fn] = read_b(slot1, fn);
+                if (fm >= FM / 2) {
+                    const int t = (fm - FM / 2) * FN + fn;
+#pragma unroll
+                    for (int q = 0; q < PER; ++q) issue(t * PER + q);
+                }
+                __builtin_amdgcn_sched_barrier(0x7);
             }
+            if (fm == FM / 2 - 1) wait_vmem_barrier();
+        }
+        if (OPS == 3) {
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) sa_cur[fm] = sa_nx[fm];
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) sb_cur[fn] = sb_nx[fn];
         }
     };
-    auto step = [&](int ks, auto ops_c) __attribute__((always_inline)) {
-        const bool more = ks + 1 < nks;
-        if (more) load_stage(ks + 1);
-        compute(ks & 1, ops_c);
-        if (more) store_stage((ks + 1) & 1);
-        __syncthreads();
-    };
 
-    load_stage(0);
-    store_stage(0);
-    load_scales(0, sa_cur, sb_cur);
-    __syncthreads();
-    for (int kb = 0; kb < nkb; ++kb) {
-        if (kb + 1 < nkb) load_scales(kb + 1, sa_nxt, sb_nxt);
-        const int ks0 = kb * 4;
+    int ks0 = 0;
+    for (; ks0 + 4 <= nks; ks0 += 4) {
         step(ks0, IntC<0>{});
-        if (ks0 + 1 < nks) step(ks0 + 1, IntC<1>{});
-        if (ks0 + 2 < nks) step(ks0 + 2, IntC<2>{});
-        if (ks0 + 3 < nks) step(ks0 + 3, IntC<3>{});
-        if (kb + 1 < nkb) {
-#pragma unroll
-            for (int fm = 0; fm < FM; ++fm) sa_cur[fm] = sa_nxt[fm];
-#pragma unroll
-            for (int fn = 0; fn < FN; ++fn) sb_cur[fn] = sb_nxt[fn];
-        }
+        step(ks0 + 1, IntC<1>{});
+        step(ks0 + 2, IntC<2>{});
+        step(ks0 + 3, IntC<3>{});
     }
+    if (ks0 < nks) step(ks0, IntC<0>{});
+    if (ks0 + 1 < nks) step(ks0 + 1, IntC<1>{});
+    if (ks0 + 2 < nks) step(ks0 + 2, IntC<2>{});
+    // the last steps' clamped reloads must land before the slot is reused or the wave ends
+    wait_vmem_barrier();
+    const int gs = nks;   // the epilogue uses slot (gs - 1) % 3, the last step's
 
-    // ---- epilogues (LDS is free: the last step ended with a barrier) ------------------
-    if constexpr (MODE == 1) {
-        // SwiGLU, then per-row amax over the tile's 128 intermediate columns
-        constexpr int FQ = FN / 2;
-        float* red = reinterpret_cast<float*>(smem + A_BYTES * 2);   // [WAVES_N][BM]
-        uint8_t* hq = smem;                                          // [BM][128] codes
-        float hv[FM][FQ][4];
-        float rmax[FM][4];
+        // ---- epilogue, in the LDS slot of the last K step -------------------------------
+        uint8_t* ep = smem + ((gs + kStages - 1) % kStages) * STAGE_BYTES;
+        if constexpr (MODE == 1) {
+            constexpr int FQ = FN / 2;
+            uint8_t* hq = ep;                                              // [BM][128] codes
+            float* red = reinterpret_cast<float*>(ep + BM * 128);         // [WAVES_N][BM]
+            float rmax[FM][4];
 #pragma unroll
-        for (int fm = 0; fm < FM; ++fm) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) rmax[fm][r] = 0.f;
-#pragma unroll
-            for (int q = 0; q < FQ; ++q) {
+            for (int fm = 0; fm < FM; ++fm) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float gt = acc[fm][q][r];
-                    const float up = acc[fm][q + FQ][r];
-                    const float h = gt / (1.0f + expf(-gt)) * up;
-                    hv[fm][q][r] = h;
-                    rmax[fm][r] = fmaxf(rmax[fm][r], fabsf(h));
+                    float m = 0.f;
+#pragma unroll
+                    for (int q = 0; q < FQ; ++q) {
+                        const float h = swiglu(acc[fm][q][r], acc[fm][q + FQ][r]);
+                        acc[fm][q][r] = h;                 // h replaces the gate sum
+                        m = fmaxf(m, fabsf(h));
+                    }
+                    m = fmaxf(m, __shfl_xor(m, 1, 64));
+                    m = fmaxf(m, __shfl_xor(m, 2, 64));
+                    m = fmaxf(m, __shfl_xor(m, 4, 64));
+                    m = fmaxf(m, __shfl_xor(m, 8, 64));
+                    rmax[fm][r] = m;
+                    if ((lane & 15) == 0) red[wn * BM + wm * WM + fm * 16 + 4 * g + r] = m;
                 }
             }
+            wait_lds_barrier();
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float m = rmax[fm][r];
-                m = fmaxf(m, __shfl_xor(m, 1, 64));
-                m = fmaxf(m, __shfl_xor(m, 2, 64));
-                m = fmaxf(m, __shfl_xor(m, 4, 64));
-                m = fmaxf(m, __shfl_xor(m, 8, 64));
-                rmax[fm][r] = m;
-                if ((lane & 15) == 0) red[wn * BM + wm * WM + fm * 16 + 4 * g + r] = m;
-            }
-        }
-        __syncthreads();
+            for (int fm = 0; fm < FM; ++fm) {
 #pragma unroll
-        for (int fm = 0; fm < FM; ++fm) {
+                for (int r = 0; r < 4; ++r) {
+                    const int rt = wm * WM + fm * 16 + 4 * g + r;
+                    float m = rmax[fm][r];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int rt = wm * WM + fm * 16 + 4 * g + r;
-                float m = red[rt];
+                    for (int w = 0; w < WAVES_N; ++w)
+                        if (w != wn) m = fmaxf(m, red[w * BM + rt]);
+                    const int byte = requant_scale_byte(m);
+                    const float mul = __uint_as_float((uint32_t)(254 - byte) << 23);  // 2^-(byte-127)
 #pragma unroll
-                for (int w = 1; w < WAVES_N; ++w) m = fmaxf(m, red[w * BM + rt]);
-                const int byte = requant_scale_byte(m);
-                const float mul = __uint_as_float((uint32_t)(254 - byte) << 23);  // 2^-(byte-127)
-#pragma unroll
-                for (int q = 0; q < FQ; q += 2) {
-                    const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(hv[fm][q][r] * mul,
-                                                                   hv[fm][q + 1][r] * mul, 0, false);
-                    const int col = 16 * (wn * FQ + q) + (lane & 15);
-                    hq[rt * 128 + col] = (uint8_t)(pk & 0xff);
-                    hq[rt * 128 + col + 16] = (uint8_t)((pk >> 8) & 0xff);
+                    for (int q = 0; q < FQ; q += 2) {
+                        const float h1 = (q + 1 < FQ) ? acc[fm][q + 1 < FQ ? q + 1 : q][r] * mul : 0.f;
+                        const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(acc[fm][q][r] * mul, h1, 0, false);
+                        const int col = 16 * (wn * FQ + q) + (lane & 15);
+                        hq[rt * 128 + col] = (uint8_t)(pk & 0xff);
+                        if (q + 1 < FQ) hq[rt * 128 + col + 16] = (uint8_t)((pk >> 8) & 0xff);
+                    }
+                    if (wn == 0 && (lane & 15) == 0)
+                        args.h_sf[(size_t)(row0 + rt) * args.h_sf_stride + nt] = (uint8_t)byte;
                 }
-                if (wn == 0 && (lane & 15) == 0)
-                    args.h_sf[(size_t)(row0 + rt) * args.h_sf_stride + nt] = (uint8_t)byte;
+            }
+            wait_lds_barrier();
+            // coalesced copy of the BM x 128 code tile
+            constexpr int CHUNKS = BM * 128 / 16;
+#pragma unroll
+            for (int c = tid; c < CHUNKS; c += kThreads) {
+                const int r = c >> 3, cc = c & 7;
+                *reinterpret_cast<v4i*>(args.h8 + (size_t)(row0 + r) * args.h_stride + nt * 128 + cc * 16) =
+                    *reinterpret_cast<const v4i*>(hq + r * 128 + cc * 16);
+            }
+        } else {
+            // weight rows by their top-k weight, round to bf16 and write each 16-row slice of
+            // the wave's tile through a private LDS area as 16-byte row chunks
+            uint16_t* wbuf = reinterpret_cast<uint16_t*>(ep + wave * (16 * WN * 2));   // [16][WN]
+            constexpr int CPR = WN / 8;                 // 16-byte chunks per row
+            constexpr int CPL = 16 * CPR / 64;          // chunks per lane
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int slot = args.perm[row0 + wm * WM + fm * 16 + 4 * g + r];
+                    const float w = slot >= 0 ? args.topk_weights[slot] : 0.f;
+#pragma unroll
+                    for (int fn = 0; fn < FN; ++fn)
+                        wbuf[(4 * g + r) * WN + fn * 16 + (lane & 15)] = f32_to_bf16_rne(acc[fm][fn][r] * w);
+                }
+                wait_lds();
+#pragma unroll
+                for (int q = 0; q < CPL; ++q) {
+                    const int c = lane + 64 * q;
+                    const int rr = c / CPR, cc = c % CPR;
+                    const int slot = args.perm[row0 + wm * WM + fm * 16 + rr];
+                    const v4i val = *reinterpret_cast<const v4i*>(wbuf + rr * WN + cc * 8);
+                    if (slot >= 0)
+                        *reinterpret_cast<v4i*>(args.stage + (size_t)slot * args.out_cols + nt * kBN +
+                                                wn * WN + cc * 8) = val;
+                }
+                wait_lds();
             }
         }
-        __syncthreads();
-        // coalesced copy of the BM x 128 code tile
-        constexpr int CHUNKS = BM * 128 / 16;
-#pragma unroll
-        for (int c = tid; c < CHUNKS; c += kThreads) {
-            const int r = c >> 3, cc = c & 7;
-            *reinterpret_cast<v4i*>(args.h8 + (size_t)(row0 + r) * args.h_stride + nt * 128 + cc * 16) =
-                *reinterpret_cast<const v4i*>(hq + r * 128 + cc * 16);
-        }
-    } else {
-        // weight by the row's top-k weight, bf16, write the slot's staging row
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int rt = wm * WM + fm * 16 + 4 * g + r;
-                const int slot = args.perm[row0 + rt];
-                if (slot < 0) continue;
-                const float w = args.topk_weights[slot];
-                uint16_t* dst = args.stage + (size_t)slot * args.out_cols + nt * kBN + wn * WN + (lane & 15);
-#pragma unroll
-                for (int fn = 0; fn < FN; ++fn) dst[fn * 16] = f32_to_bf16_rne(acc[fm][fn][r] * w);
-            }
-        }
-    }
+#endif
 }
 
+template <int BM, int WAVES_M, int WAVES_N, int MODE>
+hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
+    // one workgroup per possible tile; those past the tiles in use return at once
+    const unsigned grid = (unsigned)a.max_tiles * (unsigned)a.n_tiles;
+    grouped_gemm_kernel<BM, WAVES_M, WAVES_N, MODE><<<grid, kThreads, 0, stream>>>(a);
+    return hipGetLastError();
+}
+
+// Row-tile classes (4 waves each): 256 rows as 2x2 waves of 128x128, 128 rows as 2x2
+// waves of 64x128, 64 rows as 1x4 waves of 64x64.
 template <int MODE>
 hipError_t launch_mode(int block_m, const GemmArgs& a, hipStream_t stream) {
-    const unsigned grid = (unsigned)a.max_tiles * (unsigned)a.n_tiles;
-    if (grid == 0) return hipSuccess;
+    if (a.max_tiles == 0 || a.n_tiles == 0) return hipSuccess;
     switch (block_m) {
-        case 256: grouped_gemm_kernel<256, 2, 2, MODE><<<grid, kThreads, 0, stream>>>(a); break;
-        case 128: grouped_gemm_kernel<128, 2, 2, MODE><<<grid, kThreads, 0, stream>>>(a); break;
-        case 64: grouped_gemm_kernel<64, 1, 4, MODE><<<grid, kThreads, 0, stream>>>(a); break;
+        case 256: return launch_cfg<256, 2, 2, MODE>(a, stream);
+        case 128: return launch_cfg<128, 2, 2, MODE>(a, stream);
+        case 64: return launch_cfg<64, 1, 4, MODE>(a, stream);
         default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 }  // namespace

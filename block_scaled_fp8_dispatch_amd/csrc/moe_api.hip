@@ -2,6 +2,7 @@
 // launch sequence route -> Linear1(+SwiGLU+requant) -> Linear2(+weights) -> combine.
 // Everything is enqueued on the caller's stream; nothing here synchronises except
 // moe_read_diagnostics, and nothing allocates device memory.
+#include <cstdlib>
 #include <cstring>
 
 #include "moe_internal.h"
@@ -16,7 +17,7 @@ bool shape_ok(const moe_shape_t* s) {
     if (!s) return false;
     if (s->num_experts < 1 || s->num_experts > MOE_MAX_EXPERTS) return false;
     if (s->hidden < 256 || s->hidden % 256 != 0) return false;
-    if (s->intermediate < 128 || s->intermediate % 128 != 0) return false;
+    if (s->intermediate < 256 || s->intermediate % 128 != 0) return false;
     if (s->num_topk < 1 || s->num_topk > MOE_MAX_TOPK || s->num_topk > s->num_experts) return false;
     if (s->max_tokens < 0) return false;
     const uint64_t slots = (uint64_t)s->max_tokens * (uint64_t)s->num_topk;
@@ -30,7 +31,15 @@ bool shape_ok(const moe_shape_t* s) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Row-tile class from the mean rows per expert; MOE_BLOCK_M (64, 128 or 256) overrides it
+// for tuning.
 int choose_block_m(const moe_shape_t& s, int T) {
+    static const int forced = [] {
+        const char* v = std::getenv("MOE_BLOCK_M");
+        const int b = v ? std::atoi(v) : 0;
+        return (b == 64 || b == 128 || b == 256) ? b : 0;
+    }();
+    if (forced) return forced;
     const long avg = (long)T * s.num_topk / s.num_experts;
     if (avg >= 512) return 256;
     if (avg >= 128) return 128;

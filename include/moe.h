@@ -47,7 +47,7 @@ extern "C" {
 #endif
 
 /* Problem shape. num_experts = E local experts; hidden = H (multiple of 256);
- * intermediate = I (multiple of 128); num_topk = k (1..64); max_tokens = the largest
+ * intermediate = I (multiple of 128, at least 256); num_topk = k (1..64); max_tokens = the largest
  * num_tokens a workspace must serve (the capacity of the pages' per-rank buffer). */
 typedef struct {
     int32_t num_experts;

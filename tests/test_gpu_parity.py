@@ -44,7 +44,7 @@ def test_tiny_c0():
     (300, 5, 3, 512, 384, 1),      # 128-row tiles, ragged tails
     (700, 3, 2, 256, 640, 2),      # medium class, I not a multiple of 512
     (1200, 2, 2, 768, 256, 3),     # large class, K steps not a multiple of 4
-    (1, 4, 2, 256, 128, 4),        # one token
+    (1, 4, 2, 256, 256, 4),        # one token
 ])
 def test_small_shapes(T, E, k, H, I, seed):
     _full_check(MoEConfig("small", T=T, E=E, k=k, H=H, I=I), seed=seed)
