@@ -41,7 +41,7 @@ def parse():
     ap.add_argument("--config", default="c2")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=4)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this size first (for counter scaling)")
     return ap.parse_args()
@@ -66,8 +66,8 @@ def load_traffic(cfg_name: str):
 
 
 def cpu_baseline(inp_cpu: dict, cfg, n_tokens: int):
-    """Time the oracle on a few tokens whose top-k experts all lie in the two lowest expert
-    ids (so the sample decodes two experts' weights, not all of them)."""
+    """Time the oracle on the first n_tokens tokens of the batch (every expert they route to
+    is decoded, so the sample carries the oracle's full per-expert cost)."""
     import numpy as np
     import oracle
     try:
@@ -76,17 +76,15 @@ def cpu_baseline(inp_cpu: dict, cfg, n_tokens: int):
     except Exception:
         threads = os.cpu_count() or 1
     idx = inp_cpu["topk_idx"]
-    pool = [t for t in range(idx.shape[0]) if np.all((idx[t] >= 0) & (idx[t] < 2))]
-    if len(pool) < n_tokens:
-        pool = list(range(idx.shape[0]))
-    toks = pool[:n_tokens]
+    toks = list(range(min(n_tokens, idx.shape[0])))
     t0 = time.perf_counter()
     oracle.forward_inputs(inp_cpu, tokens=toks)
     dt = time.perf_counter() - t0
     slots = int(np.sum((idx[toks] >= 0) & (idx[toks] < cfg.E)))
+    experts = int(len(np.unique(idx[toks][(idx[toks] >= 0) & (idx[toks] < cfg.E)])))
     flop = 6.0 * slots * cfg.H * cfg.I
     return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{len(toks)} tokens ({slots} slots, experts 0-1) of {cfg.name}, "
+            "sample": f"first {len(toks)} tokens ({slots} slots over {experts} experts) of {cfg.name}, "
                       f"{dt:.1f} s; numpy fp64, BLAS threads={threads}",
             "seconds": dt}
 
