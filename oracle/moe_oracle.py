@@ -282,20 +282,32 @@ def route(topk_idx: np.ndarray, E: int, BM: int) -> Dict[str, np.ndarray]:
 # ----------------------------------------------------------------------------
 
 
-def linear1(xr: np.ndarray, w1e: np.ndarray, w1e_sf: np.ndarray, row_chunk: int = 1024):
+def linear1(xr: np.ndarray, w1e: np.ndarray, w1e_sf: np.ndarray, row_chunk: int = 1024,
+            abs_sums: bool = False):
     """G = xr . W1_gate^T, U = xr . W1_up^T for one expert, fp64 [P1 3.1 step 2; 4.2].
-    xr: dequantised activation rows [R, H]; w1e u8 [2I, H/2]; w1e_sf u8 [2I, H/32]."""
+    xr: dequantised activation rows [R, H]; w1e u8 [2I, H/2]; w1e_sf u8 [2I, H/32].
+    With abs_sums, also returns |xr| . |W1_gate|^T and |xr| . |W1_up|^T (the sums of the
+    magnitudes of the products, used by accumulation_error_bound)."""
     R, H = xr.shape
     I = w1e.shape[0] // 2
     G = np.empty((R, I))
     U = np.empty((R, I))
+    AG = np.empty((R, I)) if abs_sums else None
+    AU = np.empty((R, I)) if abs_sums else None
+    xa = np.abs(xr) if abs_sums else None
     buf = np.empty((min(row_chunk, I), H))                                # reused: bounds memory
     for r0 in range(0, I, row_chunk):
         r1 = min(I, r0 + row_chunk)
         Wg = dequant_fp4_rows(w1e[r0:r1], w1e_sf[r0:r1], H, out=buf[: r1 - r0])
         G[:, r0:r1] = xr @ Wg.T
+        if abs_sums:
+            AG[:, r0:r1] = xa @ np.abs(Wg).T
         Wu = dequant_fp4_rows(w1e[I + r0:I + r1], w1e_sf[I + r0:I + r1], H, out=buf[: r1 - r0])
         U[:, r0:r1] = xr @ Wu.T
+        if abs_sums:
+            AU[:, r0:r1] = xa @ np.abs(Wu).T
+    if abs_sums:
+        return G, U, AG, AU
     return G, U
 
 
@@ -305,9 +317,42 @@ def swiglu(g: np.ndarray, u: np.ndarray) -> np.ndarray:
         return g / (1.0 + np.exp(-g)) * u
 
 
+# Largest slope of silu(v) = v * sigmoid(v) over the reals (about 1.0998, at v ~ 2.40).
+SILU_LIPSCHITZ = 1.1
+# Unit roundoff used for FP32 arithmetic of unknown order and rounding mode: 2^-23 covers
+# rounding by truncation as well as round-to-nearest (2^-24).
+FP32_UNIT = 2.0 ** -23
+
+
+def accumulation_error_bound(g: np.ndarray, u: np.ndarray, ag: np.ndarray, au: np.ndarray,
+                             K: int) -> np.ndarray:
+    """Bound on |h32 - h| for h = silu(g) * u, where h32 is computed from g32 and u32, FP32
+    accumulations of the same K exact products in any order, and the SwiGLU is then
+    evaluated in FP32.
+
+    A sum of K terms accumulated in floating point with unit roundoff eps is within
+    gamma_{K-1} * sum|terms| of the exact sum, gamma_n = n*eps / (1 - n*eps) (the standard
+    forward error bound of recursive summation; it holds for every summation order). With
+    dg, du those bounds for g and u (ag, au are the sums of |product|):
+        |silu(g32) u32 - silu(g) u| <= L dg (|u| + du) + |silu(g)| du,   L = SILU_LIPSCHITZ,
+    and evaluating silu(g32) * u32 in FP32 (exponential, reciprocal, three products, one
+    sum: a few units each) adds at most (16 + |g|) eps of the result (the |g| term is the
+    rounding of the exponential's argument)."""
+    n = max(K - 1, 1)
+    gamma = n * FP32_UNIT / (1.0 - n * FP32_UNIT)
+    dg = gamma * ag
+    du = gamma * au
+    with np.errstate(over="ignore"):
+        sg = g / (1.0 + np.exp(-g))
+    acc = SILU_LIPSCHITZ * dg * (np.abs(u) + du) + np.abs(sg) * du
+    h_mag = (np.abs(sg) + SILU_LIPSCHITZ * dg) * (np.abs(u) + du)
+    return acc + (16.0 + np.abs(g) + dg) * FP32_UNIT * h_mag
+
+
 def forward(x_fp8, x_sf, topk_idx, topk_weights, w1, w1_sf, w2, w2_sf,
             tokens: Optional[Sequence[int]] = None, cols: Optional[Sequence[int]] = None,
-            row_chunk: int = 1024, keep_intermediates: bool = True):
+            row_chunk: int = 1024, keep_intermediates: bool = True,
+            keep_bounds: bool = False):
     """The Mega MoE forward of one device's local experts [P1 3.1-3.3; P2 5].
 
     Shapes: x_fp8 u8 [T,H]; x_sf u8 [T, >=H/128]; topk_idx i32 [T,k]; topk_weights
@@ -319,6 +364,8 @@ def forward(x_fp8, x_sf, topk_idx, topk_weights, w1, w1_sf, w2, w2_sf,
       y_bits  u16 [len(tokens), len(cols)]  bf16 bit patterns of y
       y       f64 (y before the bf16 rounding)
       h8      {slot: e4m3 codes [I]}, h_sf {slot: UE8M0 bytes [I/128]}   (if kept)
+      h, h_bound  {slot: fp64 h [I]}, {slot: accumulation_error_bound of h [I]}
+                  (if keep_bounds; otherwise empty)
     Steps, per expert e and each of its slots (t, j):
       O3  g = x[t] . W1[e, n],  u = x[t] . W1[e, I+n]        (fp64)        [P1 3.1 step 2; 4.2]
       O4  h = silu(g) * u                                                  [P1 3.1 step 3]
@@ -339,15 +386,19 @@ def forward(x_fp8, x_sf, topk_idx, topk_weights, w1, w1_sf, w2, w2_sf,
     tok_pos = {int(t): i for i, t in enumerate(toks)}
 
     contrib = np.zeros((len(toks), k, len(cols_arr)), dtype=np.float64)   # w[t,j] * o[t,j,:]
-    h8, hsf = {}, {}
+    h8, hsf, h64, hbound = {}, {}, {}, {}
     xd_all = dequant_fp8_rows(x_fp8[toks], np.asarray(x_sf)[toks], H)   # [len(toks), H]
     for e in range(E):
         slots = [(int(t), j) for t in toks for j in range(k) if int(topk_idx[t, j]) == e]
         if not slots:
             continue
         xr = np.stack([xd_all[tok_pos[t]] for t, _ in slots])            # [R, H]
-        G, U = linear1(xr, w1[e], w1_sf[e], row_chunk)
+        if keep_bounds:
+            G, U, AG, AU = linear1(xr, w1[e], w1_sf[e], row_chunk, abs_sums=True)
+        else:
+            G, U = linear1(xr, w1[e], w1_sf[e], row_chunk)
         h = swiglu(G, U)
+        hb = accumulation_error_bound(G, U, AG, AU, H) if keep_bounds else None
         q, sf, hd = requant_fp8_1x128(h)
         O = np.empty((len(slots), len(cols_arr)))                          # [R, len(cols)]
         buf = np.empty((min(row_chunk, len(cols_arr)), I))
@@ -360,11 +411,15 @@ def forward(x_fp8, x_sf, topk_idx, topk_weights, w1, w1_sf, w2, w2_sf,
             if keep_intermediates:
                 h8[t * k + j] = q[r]
                 hsf[t * k + j] = sf[r]
+            if keep_bounds:
+                h64[t * k + j] = h[r]
+                hbound[t * k + j] = hb[r]
     # O7: the combine sums the slots in order j = 0..k-1 (skipped slots add 0)
     acc = np.zeros((len(toks), len(cols_arr)), dtype=np.float64)
     for j in range(k):
         acc += contrib[:, j]
-    return dict(y=acc, y_bits=bf16_rne_bits(acc), h8=h8, h_sf=hsf, tokens=toks, cols=cols_arr)
+    return dict(y=acc, y_bits=bf16_rne_bits(acc), h8=h8, h_sf=hsf, h=h64, h_bound=hbound,
+                tokens=toks, cols=cols_arr)
 
 
 def forward_inputs(inp: dict, **kw):

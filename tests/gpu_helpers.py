@@ -77,8 +77,32 @@ def check_routing(got: dict, idx_np: np.ndarray, E: int):
     return ref
 
 
+def _e4m3_half_gap() -> np.ndarray:
+    """For each e4m3 code: half the larger of the two gaps to its neighbours on the grid
+    (the widest distance from which round-to-nearest can land on it)."""
+    pos = np.array([oracle.e4m3_value(c) for c in range(0x7F)])
+    up = np.diff(pos, append=pos[-1] + (pos[-1] - pos[-2]))
+    down = np.diff(pos, prepend=-pos[1])          # the gap below 0 is the one to -min
+    half = 0.5 * np.maximum(up, down)
+    out = np.zeros(256)
+    out[:0x7F] = half
+    out[0x80:0xFF] = half
+    out[0x7F] = out[0xFF] = np.nan
+    return out
+
+
+_HALF_GAP = _e4m3_half_gap()
+
+
 def check_intermediates(run: Run, ref: dict, inv: np.ndarray):
-    """Compare GPU h8/h_sf with the oracle's requantised intermediate slot by slot."""
+    """Compare GPU h8/h_sf with the oracle's requantised intermediate slot by slot.
+
+    Each element is decoded on both sides. Elements whose values differ count against the
+    0.1% budget. Each must be one step apart on the e4m3 grid at the coarser of the two
+    block scales, or, where the oracle returns h and its FP32 accumulation error bound,
+    the GPU's value must be a round-to-nearest result of some h' within that bound of
+    the exact h (this covers small elements of a block, where the grid is finer than the
+    FP32 error of a dot product that cancels)."""
     slots = sorted(ref["h8"].keys())
     if not slots:
         return 0.0
@@ -87,13 +111,21 @@ def check_intermediates(run: Run, ref: dict, inv: np.ndarray):
     g8, gsf = run.intermediates(rows)
     r8 = np.stack([ref["h8"][s] for s in slots])
     rsf = np.stack([ref["h_sf"][s] for s in slots])
-    I = r8.shape[1]
     gs = np.repeat(gsf, 128, axis=1)
     rs = np.repeat(rsf, 128, axis=1)
     dist = oracle.e4m3_code_distance(g8, gs, r8, rs)
     frac = float((dist > 0).mean())
-    assert dist.max() <= 1, f"intermediate off by {dist.max()} codes"
-    assert frac <= OFF_BY_ONE_MAX, f"{frac:.2e} of intermediates off by one code"
+    far = dist > 1
+    if far.any() and ref.get("h"):
+        h = np.stack([ref["h"][s] for s in slots])
+        hb = np.stack([ref["h_bound"][s] for s in slots])
+        scale = np.ldexp(1.0, gs.astype(np.int64) - 127)
+        vg = oracle.E4M3_TABLE[g8] * scale
+        within = np.abs(vg - h) <= hb + _HALF_GAP[g8] * scale
+        far &= ~within
+    assert not far.any(), (f"{int(far.sum())} intermediates further than one code and outside "
+                           f"the FP32 accumulation bound (max distance {dist.max()})")
+    assert frac <= OFF_BY_ONE_MAX, f"{frac:.2e} of intermediates differ"
     return frac
 
 

@@ -1,0 +1,202 @@
+"""GPU edge cases and exact invariants of the forward, through the C ABI.
+
+Edge cases: zero tokens, fewer tokens than the workspace capacity, every slot on one
+expert (with duplicate experts inside a token), k = E, unused (-1) and invalid expert
+ids with the diagnostic count, many experts with most of them empty.
+
+Invariants that hold bit for bit on the GPU, whatever the tolerance against the oracle:
+the same call twice gives the same bytes; permuting tokens permutes y; relabelling
+experts leaves y unchanged; doubling the top-k weights doubles y; raising every W2 scale
+byte by one doubles y; raising the scale bytes of W1's up rows by one leaves the h8 codes
+unchanged, raises every h_sf byte by one and doubles y.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from conftest import gpu_available
+from synth import MoEConfig, make_inputs
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+import block_scaled_fp8_dispatch_amd as moe  # noqa: E402
+import oracle  # noqa: E402
+from gpu_helpers import Run, check_intermediates, check_routing, check_y  # noqa: E402
+
+
+def _host(inp):
+    return {k: (v.cpu().numpy() if isinstance(v, torch.Tensor) else v)
+            for k, v in dataclasses.asdict(inp).items() if k != "cfg"}
+
+
+def _parity(run: Run, inp, T=None):
+    T = inp.x_fp8.shape[0] if T is None else T
+    y = run.forward(T=T)
+    idx = inp.topk_idx[:T].cpu().numpy()
+    got = run.routing(T)
+    ref_route = check_routing(got, idx, inp.cfg.E)
+    host = _host(inp)
+    for key in ("x_fp8", "x_sf", "topk_idx", "topk_weights"):
+        host[key] = host[key][:T]
+    ref = oracle.forward_inputs(host, keep_bounds=True)
+    check_intermediates(run, ref, got["inv"])
+    check_y(y, ref)
+    return y, ref, ref_route
+
+
+def _bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).astype(np.int16)).view(torch.bfloat16).float().numpy()
+
+
+def test_zero_tokens_writes_nothing():
+    cfg = MoEConfig("edge", T=64, E=4, k=2, H=256, I=256)
+    print(f"[edge] zero tokens {cfg}", flush=True)
+    inp = make_inputs(cfg, seed=11, device="cuda")
+    run = Run(inp)
+    run.y.fill_(0x1234)
+    moe.moe_forward(run.y, inp.x_fp8, inp.x_sf, inp.topk_idx, inp.topk_weights, 0, run.shape,
+                    run.packed, run.ws)
+    torch.cuda.synchronize()
+    assert bool((run.y == 0x1234).all())
+
+
+def test_fewer_tokens_than_capacity():
+    cfg = MoEConfig("edge", T=300, E=6, k=2, H=512, I=256)
+    print(f"[edge] T=200 of capacity 512 {cfg}", flush=True)
+    inp = make_inputs(cfg, seed=12, device="cuda")
+    run = Run(inp, max_tokens=512)
+    run.y = torch.empty(512, cfg.H, dtype=torch.int16, device="cuda")
+    _parity(run, inp, T=200)
+    assert bool((run.y[200:] == 0x7FBF).all()), "rows past num_tokens were written"
+
+
+def test_all_slots_on_one_expert_with_duplicates():
+    cfg = MoEConfig("edge", T=200, E=4, k=2, H=256, I=384)
+    print(f"[edge] all slots on expert 2 {cfg}", flush=True)
+    inp = make_inputs(cfg, seed=13, device="cuda")
+    inp = dataclasses.replace(inp, topk_idx=torch.full_like(inp.topk_idx, 2))
+    run = Run(inp)
+    _, _, r = _parity(run, inp)
+    assert list(r["counts"]) == [0, 0, 400, 0]
+
+
+def test_k_equals_num_experts():
+    cfg = MoEConfig("edge", T=96, E=3, k=3, H=256, I=256)
+    print(f"[edge] k = E {cfg}", flush=True)
+    inp = make_inputs(cfg, seed=14, device="cuda")
+    run = Run(inp)
+    _parity(run, inp)
+
+
+def test_unused_and_invalid_slots():
+    cfg = MoEConfig("edge", T=160, E=5, k=3, H=256, I=256)
+    print(f"[edge] -1 and invalid ids {cfg}", flush=True)
+    inp = make_inputs(cfg, seed=15, device="cuda")
+    idx = inp.topk_idx.cpu().numpy().copy()
+    rng = np.random.default_rng(0)
+    idx[rng.random(idx.shape) < 0.2] = -1
+    bad = rng.random(idx.shape) < 0.05
+    idx[bad] = rng.choice(np.array([5, 6, 1000, -2, -7, 2**31 - 1], dtype=np.int64),
+                          size=int(bad.sum())).astype(np.int32)
+    idx[7, :] = -1                 # a token with no slot at all
+    idx[9, :] = [5, -1, 1000]      # only invalid ids
+    inp = dataclasses.replace(inp, topk_idx=torch.from_numpy(idx).cuda())
+    run = Run(inp)
+    y, ref, r = _parity(run, inp)
+    assert (y[7] == 0).all() and (y[9] == 0).all(), "a token without valid slots is not +0"
+    invalid, counts = moe.moe_read_diagnostics(run.shape, run.ws)
+    assert invalid == int(r["num_invalid"]) == int(((idx < -1) | (idx >= cfg.E)).sum())
+    assert counts == [int(c) for c in r["counts"]]
+
+
+def test_many_experts_mostly_empty():
+    cfg = MoEConfig("edge", T=100, E=1024, k=8, H=256, I=256)
+    print(f"[edge] E=1024 {cfg}", flush=True)
+    inp = make_inputs(cfg, seed=16, device="cuda")
+    run = Run(inp)
+    _parity(run, inp)
+
+
+# ---------------------------------------------------------------------------
+# Exact invariants
+# ---------------------------------------------------------------------------
+
+CFG_INV = MoEConfig("inv", T=333, E=5, k=2, H=512, I=384)
+
+
+def _run_once(inp):
+    run = Run(inp)
+    y = run.forward()
+    return run, y
+
+
+def test_deterministic():
+    print(f"[inv] determinism {CFG_INV}", flush=True)
+    inp = make_inputs(CFG_INV, seed=21, device="cuda")
+    run = Run(inp)
+    y1 = run.forward().copy()
+    L = run.layout()
+    h1 = run.ws[L["h8"]: L["stage"]].clone()
+    y2 = run.forward()
+    h2 = run.ws[L["h8"]: L["stage"]]
+    assert np.array_equal(y1, y2)
+    rows = int(run.routing()["offsets"][-1])
+    I = CFG_INV.I
+    assert torch.equal(h1[: rows * I], h2[: rows * I])
+
+
+def test_token_permutation():
+    print(f"[inv] token permutation {CFG_INV}", flush=True)
+    inp = make_inputs(CFG_INV, seed=22, device="cuda")
+    _, y = _run_once(inp)
+    pi = torch.from_numpy(np.random.default_rng(3).permutation(CFG_INV.T)).cuda()
+    inp2 = dataclasses.replace(inp, x_fp8=inp.x_fp8[pi].contiguous(), x_sf=inp.x_sf[pi].contiguous(),
+                               topk_idx=inp.topk_idx[pi].contiguous(),
+                               topk_weights=inp.topk_weights[pi].contiguous())
+    _, y2 = _run_once(inp2)
+    assert np.array_equal(y2, y[pi.cpu().numpy()])
+
+
+def test_expert_relabelling():
+    print(f"[inv] expert relabelling {CFG_INV}", flush=True)
+    inp = make_inputs(CFG_INV, seed=23, device="cuda")
+    _, y = _run_once(inp)
+    sigma = np.array([3, 0, 4, 1, 2])           # old expert e becomes sigma[e]
+    src = torch.from_numpy(np.argsort(sigma)).cuda()   # new slot e' holds old expert src[e']
+    idx2 = torch.from_numpy(sigma[inp.topk_idx.cpu().numpy()].astype(np.int32)).cuda()
+    inp2 = dataclasses.replace(inp, topk_idx=idx2, w1=inp.w1[src].contiguous(),
+                               w1_sf=inp.w1_sf[src].contiguous(), w2=inp.w2[src].contiguous(),
+                               w2_sf=inp.w2_sf[src].contiguous())
+    _, y2 = _run_once(inp2)
+    assert np.array_equal(y2, y)
+
+
+def test_weight_and_scale_doubling():
+    print(f"[inv] doubling {CFG_INV}", flush=True)
+    inp = make_inputs(CFG_INV, seed=24, device="cuda")
+    run, y = _run_once(inp)
+    yf = _bf16(y)
+    assert np.abs(yf).max() < 1e30
+    # top-k weights x 2
+    _, y_w = _run_once(dataclasses.replace(inp, topk_weights=inp.topk_weights * 2))
+    assert np.array_equal(_bf16(y_w), 2 * yf)
+    # every W2 scale byte + 1
+    _, y_s = _run_once(dataclasses.replace(inp, w2_sf=inp.w2_sf + 1))
+    assert np.array_equal(_bf16(y_s), 2 * yf)
+    # W1 up rows' scale bytes + 1: same codes, h_sf + 1, y x 2
+    I = CFG_INV.I
+    w1_sf = inp.w1_sf.clone()
+    w1_sf[:, I:, :] += 1
+    run_u, y_u = _run_once(dataclasses.replace(inp, w1_sf=w1_sf))
+    assert np.array_equal(_bf16(y_u), 2 * yf)
+    rows = int(run.routing()["offsets"][-1])
+    perm = run.routing()["perm"]
+    valid = np.nonzero(perm >= 0)[0]
+    h8a, sfa = run.intermediates(valid)
+    h8b, sfb = run_u.intermediates(valid)
+    assert rows == int(run_u.routing()["offsets"][-1])
+    assert np.array_equal(h8a, h8b)
+    assert np.array_equal(sfb.astype(np.int32), sfa.astype(np.int32) + 1)

@@ -27,7 +27,7 @@ def _full_check(cfg: MoEConfig, seed=0, tokens=None, cols=None, max_tokens=None)
     got = run.routing()
     check_routing(got, idx, cfg.E)
     host = inp.numpy()
-    ref = oracle.forward_inputs(host, tokens=tokens, cols=cols)
+    ref = oracle.forward_inputs(host, tokens=tokens, cols=cols, keep_bounds=True)
     frac = check_intermediates(run, ref, got["inv"])
     err = check_y(y, ref, tokens=ref["tokens"] if tokens is not None else None, cols=cols)
     print(f"[parity] {cfg.name}: block_m={got['block_m']} tiles={got['meta'][0]} "

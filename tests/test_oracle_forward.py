@@ -8,6 +8,7 @@
   w=0 vs unused slot, empty experts, token/column sampling
 """
 import json
+import math
 import os
 from fractions import Fraction
 
@@ -219,3 +220,89 @@ def test_invalid_ids_are_skipped():
     b["topk_idx"][1, 0] = -1
     b["topk_idx"][3, 1] = -1
     assert np.array_equal(oracle.forward_inputs(a)["y_bits"], oracle.forward_inputs(b)["y_bits"])
+
+
+def _fp32_sums(p64: np.ndarray):
+    """FP32 accumulations of the exact products p64 [..., K] in several orders and two
+    rounding modes: sequential, reversed, pairwise (numpy), blocks of 128 then across
+    blocks, and sequential with rounding toward zero."""
+    p32 = p64.astype(np.float32)
+    assert np.array_equal(p32.astype(np.float64), p64)           # the products are exact
+    K = p64.shape[-1]
+    out = []
+    acc = np.zeros(p64.shape[:-1], np.float32)
+    for c in range(K):
+        acc = acc + p32[..., c]
+    out.append(acc)
+    acc = np.zeros(p64.shape[:-1], np.float32)
+    for c in reversed(range(K)):
+        acc = acc + p32[..., c]
+    out.append(acc)
+    out.append(np.sum(p32, axis=-1, dtype=np.float32))
+    blocks = [np.sum(p32[..., b:b + 128], axis=-1, dtype=np.float32) for b in range(0, K, 128)]
+    acc = np.zeros(p64.shape[:-1], np.float32)
+    for b in blocks:
+        acc = acc + b
+    out.append(acc)
+    acc = np.zeros(p64.shape[:-1], np.float32)
+    for c in range(K):
+        v = acc.astype(np.float64) + p64[..., c]
+        r = v.astype(np.float32)
+        over = np.abs(r.astype(np.float64)) > np.abs(v)
+        acc = np.where(over, np.nextafter(r, np.float32(0)), r)
+    out.append(acc)
+    return out
+
+
+def _bound_ratios(pg, pu, g, u):
+    """|h32 - h| / bound for every FP32 summation variant of the products pg, pu."""
+    K = pg.shape[-1]
+    h = oracle.swiglu(g, u)
+    bound = oracle.accumulation_error_bound(g, u, np.abs(pg).sum(-1), np.abs(pu).sum(-1), K)
+    out = []
+    for g32, u32 in zip(_fp32_sums(pg), _fp32_sums(pu)):
+        one = np.float32(1)
+        h32 = (g32 / (one + np.exp(-g32)) * u32).astype(np.float64)
+        out.append(np.abs(h32 - h) / bound)
+    return np.max(out, axis=0), bound, h
+
+
+def test_accumulation_error_bound_on_the_path_operands():
+    """The bound holds for products of e4m3 activations and E2M1 weights as the path
+    makes them, summed in FP32 in several orders and rounding modes, then an FP32 SwiGLU;
+    and it stays far below the size of h."""
+    K, R, N = 512, 16, 16
+    inp = _small(T=R, E=1, k=1, H=K, I=128, seed=3)
+    x = oracle.dequant_fp8_rows(inp["x_fp8"], inp["x_sf"], K)                  # [R, K]
+    w = oracle.dequant_fp4_rows(inp["w1"][0], inp["w1_sf"][0], K)             # [256, K]
+    pg = x[:, None, :] * w[None, :N, :]
+    pu = x[:, None, :] * w[None, 128:128 + N, :]
+    ratio, bound, h = _bound_ratios(pg, pu, pg.sum(-1), pu.sum(-1))
+    assert np.all(ratio <= 1.0), ratio.max()
+    assert np.median(bound) < 1e-3 * np.abs(h).max()
+
+
+def test_accumulation_error_bound_is_sharp_on_adversarial_sums():
+    """The bound covers arbitrary FP32 terms (it is a statement about any exactly
+    representable products), and adversarial sums come within a small factor of it, so
+    that neither of its two error paths nor the growth with K can be dropped. Columns 0-3
+    cancel in the up projection, columns 4-7 in the gate projection: positive terms in
+    [0.5, 1) on the first K half and the same terms negated on the second, so a sequential
+    sum climbs to its largest value before cancelling to an exact 0 and keeps the rounding
+    errors of the climb (most of all when rounding toward zero)."""
+    K, R, N = 512, 4, 8
+    rng = np.random.default_rng(11)
+    half = K // 2
+    pg = rng.standard_normal((R, N, K)).astype(np.float32).astype(np.float64)
+    pu = rng.standard_normal((R, N, K)).astype(np.float32).astype(np.float64)
+    for p, cols in ((pu, slice(0, 4)), (pg, slice(4, 8))):
+        pos = rng.uniform(0.5, 1.0, (R, 4, half)).astype(np.float32).astype(np.float64)
+        p[:, cols, :half] = pos
+        p[:, cols, half:] = -pos
+    g = np.array([[math.fsum(v) for v in row] for row in pg])
+    u = np.array([[math.fsum(v) for v in row] for row in pu])
+    assert np.all(u[:, :4] == 0) and np.all(g[:, 4:] == 0)
+    ratio, _, _ = _bound_ratios(pg, pu, g, u)
+    assert np.all(ratio <= 1.0), ratio.max()
+    # u = 0 leaves silu(g) * du; g = 0 leaves silu'(0) * dg * u
+    assert ratio[:, :4].max() > 0.02 and ratio[:, 4:].max() > 0.02, ratio.max(axis=0)
