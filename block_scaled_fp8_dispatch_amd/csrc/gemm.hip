@@ -59,9 +59,14 @@ struct IntC {
 #define MOE_LPTR(p) ((__attribute__((address_space(3))) void*)(p))
 
 // Wait for this wave's outstanding vector-memory operations (the direct-to-LDS tile loads
-// included), then meet the other waves. One asm statement with a memory clobber, so no
-// LDS access is moved across it.
-__device__ inline void wait_vmem_barrier() { asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory"); }
+// included), then meet the other waves. The asm statement (with a memory clobber, so no
+// LDS access moves across it) does the wait; the builtin wait before it tells the
+// compiler's own wait tracking that every earlier load has landed, so it adds no waits of
+// its own further on (it would otherwise wait on the tile loads issued after this point).
+__device__ inline void wait_vmem_barrier() {
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0); expcnt, lgkmcnt left at their maximum
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+}
 // Wait for this wave's LDS accesses, then meet the other waves.
 __device__ inline void wait_lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 // Meet the other waves (every LDS value this wave read has already been consumed).
@@ -91,6 +96,31 @@ __device__ inline int requant_scale_byte(float amax) {
 __device__ inline float swiglu(float g, float u) {
     const float e = __builtin_amdgcn_exp2f(-g * 1.4426950408889634f);
     return g * u * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// acc += A x B with one UE8M0 scale byte per lane and operand, the byte chosen by OPS
+// (scale word byte OPS): v_mfma_scale_f32_16x16x128_f8f6f4 with A e4m3 (format 0), B E2M1
+// (format 4, 4 registers), FP32 accumulators held in AGPRs and updated in place. Written
+// as asm so that the accumulators stay tied to their registers (the builtin lets the
+// register allocator rotate 256 accumulators through spare registers every K step). The
+// compiler does not pad asm for MFMA hazards, so the kernel keeps them by construction:
+// the A, B and scale operands are only ever written by LDS or buffer loads (never by a
+// VALU instruction), and explicit s_nop padding separates the accumulators' VALU
+// initialisation from the first MFMA and the last MFMA from the epilogue's reads.
+template <int OPS>
+__device__ inline void mfma_scaled(v4f& acc, const v8i& a, const v4i& b, uint32_t sa, uint32_t sb) {
+    if constexpr (OPS == 0)
+        asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0] blgp:4"
+                     : "+a"(acc) : "v"(a), "v"(b), "v"(sa), "v"(sb));
+    else if constexpr (OPS == 1)
+        asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel:[1,1,0] op_sel_hi:[0,0,0] blgp:4"
+                     : "+a"(acc) : "v"(a), "v"(b), "v"(sa), "v"(sb));
+    else if constexpr (OPS == 2)
+        asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[1,1,0] blgp:4"
+                     : "+a"(acc) : "v"(a), "v"(b), "v"(sa), "v"(sb));
+    else
+        asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel:[1,1,0] op_sel_hi:[1,1,0] blgp:4"
+                     : "+a"(acc) : "v"(a), "v"(b), "v"(sa), "v"(sb));
 }
 
 template <int BM, int WAVES_M, int WAVES_N, int MODE>
@@ -235,10 +265,15 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = (v4f){0.f, 0.f, 0.f, 0.f};
+        for (int fn = 0; fn < FN; ++fn) {
+            acc[fm][fn] = (v4f){0.f, 0.f, 0.f, 0.f};
+            asm volatile("" : "+a"(acc[fm][fn]));
+        }
+    asm volatile("s_nop 7" ::: "memory");   // accumulator writes -> first MFMA
     v4i bq[FN];
     v8i a_cur, a_nx;
-    uint32_t sa_cur[FM], sb_cur[FN], sa_nx[FM], sb_nx[FN];
+    // scale words of two consecutive 4-step blocks: set (ks / 4) % 2 serves step ks
+    uint32_t sa[2][FM], sb[2][FN];
 
     // prologue: K steps 0 and 1
 #pragma unroll
@@ -246,7 +281,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
 #pragma unroll
     for (int j = 0; j < DMA; ++j) dma_one(1, 1, j);
 #pragma unroll
-    for (int i = 0; i < FM + FN; ++i) scale_one(0, i, sa_cur, sb_cur);
+    for (int i = 0; i < FM + FN; ++i) scale_one(0, i, sa[0], sb[0]);
     wait_vmem_barrier();
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) bq[fn] = read_b(0, fn);
@@ -258,12 +293,14 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
     // MFMA of the fragment before it. Half way: barrier (this wave's loads of step ks+1 have
     // landed, every wave is past step ks-1); in the second half, the loads of step ks+2
     // (clamped to the last step: a harmless reload into a free slot) and, in the third step
-    // of each 4-step block, the scale words of the next block (needed only after the next
-    // barrier, which waits for them) go one or a few per MFMA. The last A fragment's MFMAs
-    // reload each B fragment register with the next step's fragment right after its last
-    // use, and the next step's first A fragment is read with them: no double buffers.
-    auto step = [&](int ks, auto ops_c) __attribute__((always_inline)) {
+    // of each 4-step block, the scale words of the next block into the other scale set
+    // (needed only after the next barrier, which waits for them) go one or a few per MFMA.
+    // The last A fragment's MFMAs reload each B fragment register with the next step's
+    // fragment right after its last use, and the next step's first A fragment is read with
+    // them: no double buffers.
+    auto step = [&](int ks, auto ops_c, auto set_c) __attribute__((always_inline)) {
         constexpr int OPS = decltype(ops_c)::value;
+        constexpr int SET = decltype(set_c)::value;
         constexpr int HALF = FM / 2 * FN;
         constexpr int NOPS = DMA + (OPS == 2 ? FM + FN : 0);
         constexpr int PER = (NOPS + HALF - 1) / HALF;
@@ -273,16 +310,14 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
         const int ks2 = min(ks + 2, nks - 1);
         auto issue = [&](int op) __attribute__((always_inline)) {
             if (op < DMA) dma_one(ks2, slot2, op);
-            else if (op < NOPS) scale_one(ks2, op - DMA, sa_nx, sb_nx);
+            else if (op < NOPS) scale_one(ks2, op - DMA, sa[SET ^ 1], sb[SET ^ 1]);
         };
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) {
             a_cur = a_nx;
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn) {
-                const v8i b = {bq[fn].x, bq[fn].y, bq[fn].z, bq[fn].w, 0, 0, 0, 0};
-                acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    a_cur, b, acc[fm][fn], 0, 4, OPS, (int)sa_cur[fm], OPS, (int)sb_cur[fn]);
+                mfma_scaled<OPS>(acc[fm][fn], a_cur, bq[fn], sa[SET][fm], sb[SET][fn]);
                 if (fn == 0) a_nx = fm + 1 < FM ? read_a(slot, fm + 1) : read_a(slot1, 0);
                 if (fm == FM - 1) bq[fn] = read_b(slot1, fn);
                 if (fm >= FM / 2) {
@@ -294,26 +329,30 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
             }
             if (fm == FM / 2 - 1) wait_vmem_barrier();
         }
-        if (OPS == 3) {
-#pragma unroll
-            for (int fm = 0; fm < FM; ++fm) sa_cur[fm] = sa_nx[fm];
-#pragma unroll
-            for (int fn = 0; fn < FN; ++fn) sb_cur[fn] = sb_nx[fn];
-        }
     };
 
+    // 8 steps per iteration: two 4-step scale blocks, one per scale set
     int ks0 = 0;
-    for (; ks0 + 4 <= nks; ks0 += 4) {
-        step(ks0, IntC<0>{});
-        step(ks0 + 1, IntC<1>{});
-        step(ks0 + 2, IntC<2>{});
-        step(ks0 + 3, IntC<3>{});
+    for (; ks0 + 8 <= nks; ks0 += 8) {
+        step(ks0, IntC<0>{}, IntC<0>{});
+        step(ks0 + 1, IntC<1>{}, IntC<0>{});
+        step(ks0 + 2, IntC<2>{}, IntC<0>{});
+        step(ks0 + 3, IntC<3>{}, IntC<0>{});
+        step(ks0 + 4, IntC<0>{}, IntC<1>{});
+        step(ks0 + 5, IntC<1>{}, IntC<1>{});
+        step(ks0 + 6, IntC<2>{}, IntC<1>{});
+        step(ks0 + 7, IntC<3>{}, IntC<1>{});
     }
-    if (ks0 < nks) step(ks0, IntC<0>{});
-    if (ks0 + 1 < nks) step(ks0 + 1, IntC<1>{});
-    if (ks0 + 2 < nks) step(ks0 + 2, IntC<2>{});
+    if (ks0 < nks) step(ks0, IntC<0>{}, IntC<0>{});
+    if (ks0 + 1 < nks) step(ks0 + 1, IntC<1>{}, IntC<0>{});
+    if (ks0 + 2 < nks) step(ks0 + 2, IntC<2>{}, IntC<0>{});
+    if (ks0 + 3 < nks) step(ks0 + 3, IntC<3>{}, IntC<0>{});
+    if (ks0 + 4 < nks) step(ks0 + 4, IntC<0>{}, IntC<1>{});
+    if (ks0 + 5 < nks) step(ks0 + 5, IntC<1>{}, IntC<1>{});
+    if (ks0 + 6 < nks) step(ks0 + 6, IntC<2>{}, IntC<1>{});
     // the last steps' clamped reloads must land before the slot is reused or the wave ends
     wait_vmem_barrier();
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");   // last MFMA -> reads of acc
     const int gs = nks;   // the epilogue uses slot (gs - 1) % 3, the last step's
 
         // ---- epilogue, in the LDS slot of the last K step -------------------------------
