@@ -81,15 +81,24 @@ __device__ inline uint16_t f32_to_bf16_rne(float v) {
 }
 
 // UE8M0 byte for a block whose largest magnitude is `amax` (fp32): the smallest s with
-// amax <= 448 * 2^s, stored as s + 127 and clamped at 0; amax == 0 gives 127.
+// amax <= 448 * 2^s, stored as s + 127 and clamped at 0; amax == 0 gives 127. Branch-free.
 __device__ inline int requant_scale_byte(float amax) {
     const uint32_t bits = __float_as_uint(amax);
     const int ex = (int)((bits >> 23) & 0xffu);
     const uint32_t mant = bits & 0x7fffffu;
-    if (amax == 0.f) return 127;
-    if (ex == 0) return 0;
-    const int b = ex - 8 + (mant > 0x600000u ? 1 : 0);  // 448 = 1.75 * 2^8
-    return b < 0 ? 0 : b;
+    int b = ex - 8 + (mant > 0x600000u ? 1 : 0);   // 448 = 1.75 * 2^8
+    b = b < 0 ? 0 : b;                              // also covers subnormal amax (ex == 0)
+    return amax == 0.f ? 127 : b;
+}
+
+// Largest value over the 16 lanes of a DPP row (lanes 16r .. 16r+15), in every lane:
+// swap neighbours, swap pairs, mirror each half row, mirror the row.
+__device__ inline float row16_max(float m) {
+    m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0xB1, 0xF, 0xF, false)));
+    m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x4E, 0xF, 0xF, false)));
+    m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x141, 0xF, 0xF, false)));
+    m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x140, 0xF, 0xF, false)));
+    return m;
 }
 
 // silu(g) * u = g * u / (1 + e^-g), with the hardware exp2 and reciprocal (about 1 ulp each)
@@ -137,7 +146,7 @@ struct Cfg {
     static_assert(WAVES_M * WAVES_N == 4, "4 waves");
     static_assert(FM >= 2 && FM % 2 == 0, "mid-step split");
     static_assert(MODE != 1 || WAVES_N * (FN / 2) == 8, "gate/up pairing");
-    static_assert(MODE != 1 || BM * 128 + 4 * WAVES_N * BM <= STAGE_BYTES, "epilogue fits a slot");
+    static_assert(MODE != 1 || 4 * WAVES_N * BM <= STAGE_BYTES, "epilogue fits a slot");
     static_assert(MODE != 2 || 4 * 16 * WN * 2 <= STAGE_BYTES, "epilogue fits a slot");
 };
 
@@ -358,9 +367,14 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
         // ---- epilogue, in the LDS slot of the last K step -------------------------------
         uint8_t* ep = smem + ((gs + kStages - 1) % kStages) * STAGE_BYTES;
         if constexpr (MODE == 1) {
+            // Lane column l of the wave's gate fragment wn*FQ + q holds h column
+            // col0 + q (the packed W1 interleaves its rows so), up fragment FQ + q the matching
+            // up sum. Per row: h = silu(gate) * up, the largest |h| over the 128-block (lane,
+            // DPP row, then the WAVES_N waves through LDS), the UE8M0 byte and the e4m3 codes,
+            // stored as one word per lane and row.
             constexpr int FQ = FN / 2;
-            uint8_t* hq = ep;                                              // [BM][128] codes
-            float* red = reinterpret_cast<float*>(ep + BM * 128);         // [WAVES_N][BM]
+            const int l = lane & 15;
+            float* red = reinterpret_cast<float*>(ep);                    // [WAVES_N][BM]
             float rmax[FM][4];
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm) {
@@ -373,15 +387,15 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
                         acc[fm][q][r] = h;                 // h replaces the gate sum
                         m = fmaxf(m, fabsf(h));
                     }
-                    m = fmaxf(m, __shfl_xor(m, 1, 64));
-                    m = fmaxf(m, __shfl_xor(m, 2, 64));
-                    m = fmaxf(m, __shfl_xor(m, 4, 64));
-                    m = fmaxf(m, __shfl_xor(m, 8, 64));
+                    m = row16_max(m);
                     rmax[fm][r] = m;
-                    if ((lane & 15) == 0) red[wn * BM + wm * WM + fm * 16 + 4 * g + r] = m;
+                    if (l == 0) red[wn * BM + wm * WM + fm * 16 + 4 * g + r] = m;
                 }
             }
             wait_lds_barrier();
+            const int fw = wn * FQ;                                      // first gate fragment
+            const int col0 = 64 * (fw >> 2) + 4 * l + (fw & 3);
+            uint8_t* hbase = args.h8 + (size_t)row0 * args.h_stride + nt * 128 + col0;
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm) {
 #pragma unroll
@@ -393,26 +407,17 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
                         if (w != wn) m = fmaxf(m, red[w * BM + rt]);
                     const int byte = requant_scale_byte(m);
                     const float mul = __uint_as_float((uint32_t)(254 - byte) << 23);  // 2^-(byte-127)
-#pragma unroll
-                    for (int q = 0; q < FQ; q += 2) {
-                        const float h1 = (q + 1 < FQ) ? acc[fm][q + 1 < FQ ? q + 1 : q][r] * mul : 0.f;
-                        const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(acc[fm][q][r] * mul, h1, 0, false);
-                        const int col = 16 * (wn * FQ + q) + (lane & 15);
-                        hq[rt * 128 + col] = (uint8_t)(pk & 0xff);
-                        if (q + 1 < FQ) hq[rt * 128 + col + 16] = (uint8_t)((pk >> 8) & 0xff);
+                    uint8_t* dst = hbase + (size_t)rt * args.h_stride;
+                    int pk = __builtin_amdgcn_cvt_pk_fp8_f32(acc[fm][0][r] * mul, acc[fm][1][r] * mul, 0, false);
+                    if constexpr (FQ == 4) {
+                        pk = __builtin_amdgcn_cvt_pk_fp8_f32(acc[fm][2][r] * mul, acc[fm][3][r] * mul, pk, true);
+                        *reinterpret_cast<uint32_t*>(dst) = (uint32_t)pk;
+                    } else {
+                        *reinterpret_cast<uint16_t*>(dst) = (uint16_t)pk;
                     }
-                    if (wn == 0 && (lane & 15) == 0)
+                    if (wn == 0 && l == 0)
                         args.h_sf[(size_t)(row0 + rt) * args.h_sf_stride + nt] = (uint8_t)byte;
                 }
-            }
-            wait_lds_barrier();
-            // coalesced copy of the BM x 128 code tile
-            constexpr int CHUNKS = BM * 128 / 16;
-#pragma unroll
-            for (int c = tid; c < CHUNKS; c += kThreads) {
-                const int r = c >> 3, cc = c & 7;
-                *reinterpret_cast<v4i*>(args.h8 + (size_t)(row0 + r) * args.h_stride + nt * 128 + cc * 16) =
-                    *reinterpret_cast<const v4i*>(hq + r * 128 + cc * 16);
             }
         } else {
             // weight rows by their top-k weight, round to bf16 and write each 16-row slice of

@@ -12,6 +12,11 @@
 //
 //   W1 data   [E][I/128][H/128][16 frag][64 lane][16 B]   frag 0..7 gate, 8..15 up rows of
 //                                                         one 128-wide block of I
+// W1's output rows are interleaved inside each 128-block: lane column j of gate fragment f
+// (and of up fragment 8 + f) is row 64*(f/4) + 4*j + f%4 of the block. A wave that owns gate
+// fragments 4w..4w+3 (or 2w, 2w+1) then holds 4 (or 2) consecutive h columns per lane, which
+// it stores as one word. The rows of a dot product are independent, so any order is valid;
+// this one serves both wave layouts of the Linear1 kernel.
 //   W1 scales [E][I/128][ceil(H/512)][16][64] u32
 //   W2 data   [E][H/256][I/128][16][64][16 B]             frag f = rows 256*nt + 16 f ..
 //   W2 scales [E][H/256][ceil(I/512)][16][64] u32
@@ -21,6 +26,12 @@
 
 namespace moe {
 namespace {
+
+// W1 row (of 2I) held by lane column lane%16 of fragment f in column tile nt
+__device__ inline int l1_row(int f, int lane, int nt, int I) {
+    const int ff = f & 7;
+    return (f < 8 ? 0 : I) + nt * 128 + 64 * (ff >> 2) + 4 * (lane & 15) + (ff & 3);
+}
 
 // One thread per 16-byte chunk of packed data.
 __global__ __launch_bounds__(256) void pack_data_kernel(
@@ -35,9 +46,7 @@ __global__ __launch_bounds__(256) void pack_data_kernel(
     rest /= nks;
     const int nt = (int)(rest % n_tiles);
     const int e = (int)(rest / n_tiles);
-    int row;
-    if (l1_gate_up) row = (f < 8 ? 0 : I) + nt * 128 + (f & 7) * 16 + (lane & 15);
-    else row = nt * 256 + f * 16 + (lane & 15);
+    const int row = l1_gate_up ? l1_row(f, lane, nt, I) : nt * 256 + f * 16 + (lane & 15);
     const uint8_t* s = src + ((size_t)e * rows_per_expert + row) * src_row_bytes + ks * 64 +
                        (lane >> 4) * 16;
     *reinterpret_cast<uint4*>(dst + idx * 16) = *reinterpret_cast<const uint4*>(s);
@@ -56,9 +65,7 @@ __global__ __launch_bounds__(256) void pack_scale_kernel(
     rest /= nkb;
     const int nt = (int)(rest % n_tiles);
     const int e = (int)(rest / n_tiles);
-    int row;
-    if (l1_gate_up) row = (f < 8 ? 0 : I) + nt * 128 + (f & 7) * 16 + (lane & 15);
-    else row = nt * 256 + f * 16 + (lane & 15);
+    const int row = l1_gate_up ? l1_row(f, lane, nt, I) : nt * 256 + f * 16 + (lane & 15);
     const uint8_t* s = src_sf + ((size_t)e * rows_per_expert + row) * sf_row_bytes;
     uint32_t w = 0;
     for (int b = 0; b < 4; ++b) {
