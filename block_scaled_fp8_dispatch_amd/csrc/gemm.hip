@@ -73,13 +73,6 @@ __device__ inline void wait_lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n
 __device__ inline void plain_barrier() { asm volatile("s_barrier" ::: "memory"); }
 __device__ inline void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-__device__ inline uint16_t f32_to_bf16_rne(float v) {
-    uint32_t b = __float_as_uint(v);
-    if ((b & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;  // NaN
-    b += 0x7fffu + ((b >> 16) & 1u);
-    return (uint16_t)(b >> 16);
-}
-
 // UE8M0 byte for a block whose largest magnitude is `amax` (fp32): the smallest s with
 // amax <= 448 * 2^s, stored as s + 127 and clamped at 0; amax == 0 gives 127. Branch-free.
 __device__ inline int requant_scale_byte(float amax) {
@@ -147,7 +140,7 @@ struct Cfg {
     static_assert(FM >= 2 && FM % 2 == 0, "mid-step split");
     static_assert(MODE != 1 || WAVES_N * (FN / 2) == 8, "gate/up pairing");
     static_assert(MODE != 1 || 4 * WAVES_N * BM <= STAGE_BYTES, "epilogue fits a slot");
-    static_assert(MODE != 2 || 4 * 16 * WN * 2 <= STAGE_BYTES, "epilogue fits a slot");
+    static_assert(MODE != 2 || FN == 8 || FN == 4, "one 16- or 8-byte store per row");
 };
 
 template <int BM, int WAVES_M, int WAVES_N, int MODE>
@@ -420,33 +413,46 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
                 }
             }
         } else {
-            // weight rows by their top-k weight, round to bf16 and write each 16-row slice of
-            // the wave's tile through a private LDS area as 16-byte row chunks
-            uint16_t* wbuf = reinterpret_cast<uint16_t*>(ep + wave * (16 * WN * 2));   // [16][WN]
-            constexpr int CPR = WN / 8;                 // 16-byte chunks per row
-            constexpr int CPL = 16 * CPR / 64;          // chunks per lane
+            // Lane column l of the wave's fragments wn*FN .. wn*FN+FN-1 holds output columns
+            // col0 .. col0+FN-1 (the packed W2 interleaves its rows so). Each row is scaled by
+            // its slot's top-k weight, rounded to bf16 (round to nearest even) and stored as
+            // one FN*2-byte chunk per lane into the stage row of its slot; padding rows are
+            // skipped. All slot and weight loads are issued before any is needed.
+            typedef float v2f __attribute__((ext_vector_type(2)));
+            typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+            const int l = lane & 15;
+            const int fw = wn * FN;
+            const int col0 = 128 * (fw >> 3) + 8 * l + (fw & 7);
+            int slot[FM][4];
+            float wt[FM][4];
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) slot[fm][r] = args.perm[row0 + wm * WM + fm * 16 + 4 * g + r];
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    wt[fm][r] = args.topk_weights[slot[fm][r] >= 0 ? slot[fm][r] : 0];
+            uint16_t* sbase = args.stage + nt * kBN + col0;
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int slot = args.perm[row0 + wm * WM + fm * 16 + 4 * g + r];
-                    const float w = slot >= 0 ? args.topk_weights[slot] : 0.f;
+                    uint32_t pk[FN / 2];
 #pragma unroll
-                    for (int fn = 0; fn < FN; ++fn)
-                        wbuf[(4 * g + r) * WN + fn * 16 + (lane & 15)] = f32_to_bf16_rne(acc[fm][fn][r] * w);
+                    for (int p = 0; p < FN / 2; ++p) {
+                        const v2f x = {acc[fm][2 * p][r] * wt[fm][r], acc[fm][2 * p + 1][r] * wt[fm][r]};
+                        pk[p] = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, v2bf));
+                    }
+                    if (slot[fm][r] >= 0) {
+                        uint16_t* dst = sbase + (size_t)slot[fm][r] * args.out_cols;
+                        if constexpr (FN == 8)
+                            *reinterpret_cast<v4i*>(dst) = (v4i){(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3]};
+                        else
+                            *reinterpret_cast<uint2*>(dst) = make_uint2(pk[0], pk[1]);
+                    }
                 }
-                wait_lds();
-#pragma unroll
-                for (int q = 0; q < CPL; ++q) {
-                    const int c = lane + 64 * q;
-                    const int rr = c / CPR, cc = c % CPR;
-                    const int slot = args.perm[row0 + wm * WM + fm * 16 + rr];
-                    const v4i val = *reinterpret_cast<const v4i*>(wbuf + rr * WN + cc * 8);
-                    if (slot >= 0)
-                        *reinterpret_cast<v4i*>(args.stage + (size_t)slot * args.out_cols + nt * kBN +
-                                                wn * WN + cc * 8) = val;
-                }
-                wait_lds();
             }
         }
 #endif

@@ -17,8 +17,11 @@
 // fragments 4w..4w+3 (or 2w, 2w+1) then holds 4 (or 2) consecutive h columns per lane, which
 // it stores as one word. The rows of a dot product are independent, so any order is valid;
 // this one serves both wave layouts of the Linear1 kernel.
+// W2's output rows are interleaved the same way inside each 256-row tile: lane column j of
+// fragment f is row 128*(f/8) + 8*j + f%8, so a wave owning fragments 8w..8w+7 (or
+// 4w..4w+3) holds 8 (or 4) consecutive output columns per lane.
 //   W1 scales [E][I/128][ceil(H/512)][16][64] u32
-//   W2 data   [E][H/256][I/128][16][64][16 B]             frag f = rows 256*nt + 16 f ..
+//   W2 data   [E][H/256][I/128][16][64][16 B]             256 rows of H per column tile
 //   W2 scales [E][H/256][ceil(I/512)][16][64] u32
 // Every byte of the input lands in exactly one place; scale bytes of K steps past the
 // end of K are zero.
@@ -31,6 +34,11 @@ namespace {
 __device__ inline int l1_row(int f, int lane, int nt, int I) {
     const int ff = f & 7;
     return (f < 8 ? 0 : I) + nt * 128 + 64 * (ff >> 2) + 4 * (lane & 15) + (ff & 3);
+}
+
+// W2 row (of H) held by lane column lane%16 of fragment f in column tile nt
+__device__ inline int l2_row(int f, int lane, int nt) {
+    return nt * 256 + 128 * (f >> 3) + 8 * (lane & 15) + (f & 7);
 }
 
 // One thread per 16-byte chunk of packed data.
@@ -46,7 +54,7 @@ __global__ __launch_bounds__(256) void pack_data_kernel(
     rest /= nks;
     const int nt = (int)(rest % n_tiles);
     const int e = (int)(rest / n_tiles);
-    const int row = l1_gate_up ? l1_row(f, lane, nt, I) : nt * 256 + f * 16 + (lane & 15);
+    const int row = l1_gate_up ? l1_row(f, lane, nt, I) : l2_row(f, lane, nt);
     const uint8_t* s = src + ((size_t)e * rows_per_expert + row) * src_row_bytes + ks * 64 +
                        (lane >> 4) * 16;
     *reinterpret_cast<uint4*>(dst + idx * 16) = *reinterpret_cast<const uint4*>(s);
@@ -65,7 +73,7 @@ __global__ __launch_bounds__(256) void pack_scale_kernel(
     rest /= nkb;
     const int nt = (int)(rest % n_tiles);
     const int e = (int)(rest / n_tiles);
-    const int row = l1_gate_up ? l1_row(f, lane, nt, I) : nt * 256 + f * 16 + (lane & 15);
+    const int row = l1_gate_up ? l1_row(f, lane, nt, I) : l2_row(f, lane, nt);
     const uint8_t* s = src_sf + ((size_t)e * rows_per_expert + row) * sf_row_bytes;
     uint32_t w = 0;
     for (int b = 0; b < 4; ++b) {
