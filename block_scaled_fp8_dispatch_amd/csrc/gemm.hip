@@ -84,14 +84,20 @@ __device__ inline int requant_scale_byte(float amax) {
     return amax == 0.f ? 127 : b;
 }
 
-// Largest value over the 16 lanes of a DPP row (lanes 16r .. 16r+15), in every lane:
-// swap neighbours, swap pairs, mirror each half row, mirror the row.
-__device__ inline float row16_max(float m) {
-    m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0xB1, 0xF, 0xF, false)));
-    m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x4E, 0xF, 0xF, false)));
-    m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x141, 0xF, 0xF, false)));
-    m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x140, 0xF, 0xF, false)));
-    return m;
+// Largest of four non-negative floats over the 16 lanes of a DPP row (lanes 16r .. 16r+15),
+// in every lane, for four rows at once: swap neighbours, swap pairs, mirror each half row,
+// mirror the row. The values are compared as their bit patterns (non-negative floats order
+// like their bits), which needs no NaN canonicalisation; the four independent chains fill
+// each other's DPP wait states.
+__device__ inline void row16_max4(uint32_t (&m)[4]) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) m[r] = max(m[r], (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m[r], 0xB1, 0xF, 0xF, false));
+#pragma unroll
+    for (int r = 0; r < 4; ++r) m[r] = max(m[r], (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m[r], 0x4E, 0xF, 0xF, false));
+#pragma unroll
+    for (int r = 0; r < 4; ++r) m[r] = max(m[r], (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m[r], 0x141, 0xF, 0xF, false));
+#pragma unroll
+    for (int r = 0; r < 4; ++r) m[r] = max(m[r], (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m[r], 0x140, 0xF, 0xF, false));
 }
 
 // silu(g) * u = g * u / (1 + e^-g), with the hardware exp2 and reciprocal (about 1 ulp each)
@@ -367,22 +373,24 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
             // stored as one word per lane and row.
             constexpr int FQ = FN / 2;
             const int l = lane & 15;
-            float* red = reinterpret_cast<float*>(ep);                    // [WAVES_N][BM]
-            float rmax[FM][4];
+            uint32_t* red = reinterpret_cast<uint32_t*>(ep);              // [WAVES_N][BM] |h| bits
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm) {
+                uint32_t m[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    float m = 0.f;
+                    m[r] = 0u;
 #pragma unroll
                     for (int q = 0; q < FQ; ++q) {
                         const float h = swiglu(acc[fm][q][r], acc[fm][q + FQ][r]);
                         acc[fm][q][r] = h;                 // h replaces the gate sum
-                        m = fmaxf(m, fabsf(h));
+                        m[r] = max(m[r], __float_as_uint(h) & 0x7fffffffu);
                     }
-                    m = row16_max(m);
-                    rmax[fm][r] = m;
-                    if (l == 0) red[wn * BM + wm * WM + fm * 16 + 4 * g + r] = m;
+                }
+                row16_max4(m);
+                if (l == 0) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) red[wn * BM + wm * WM + fm * 16 + 4 * g + r] = m[r];
                 }
             }
             wait_lds_barrier();
@@ -394,11 +402,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int rt = wm * WM + fm * 16 + 4 * g + r;
-                    float m = rmax[fm][r];
+                    uint32_t mb = red[rt];
 #pragma unroll
-                    for (int w = 0; w < WAVES_N; ++w)
-                        if (w != wn) m = fmaxf(m, red[w * BM + rt]);
-                    const int byte = requant_scale_byte(m);
+                    for (int w = 1; w < WAVES_N; ++w) mb = max(mb, red[w * BM + rt]);
+                    const int byte = requant_scale_byte(__uint_as_float(mb));
                     const float mul = __uint_as_float((uint32_t)(254 - byte) << 23);  // 2^-(byte-127)
                     uint8_t* dst = hbase + (size_t)rt * args.h_stride;
                     int pk = __builtin_amdgcn_cvt_pk_fp8_f32(acc[fm][0][r] * mul, acc[fm][1][r] * mul, 0, false);
