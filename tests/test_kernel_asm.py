@@ -77,7 +77,11 @@ def _loops(asm):
     out = []
     for i, line in enumerate(asm):
         if "Inner Loop Header" in line:
-            label = line.split(":")[0]
+            # the marker follows the block label, on its line or on the next one
+            j = i
+            while j > 0 and not asm[j].split(";")[0].strip().endswith(":"):
+                j -= 1
+            label = asm[j].split(":")[0]
             for j in range(i + 1, len(asm)):
                 if asm[j].startswith("s_cbranch") and asm[j].split()[-1] == label:
                     out.append((i, j))
