@@ -169,15 +169,34 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
     const int g = lane >> 4;
 
     // ---- tile id -> (row tile, column tile), XCD-aware ----------------------------------
+    // Tile ids walk groups of kGroupM row tiles across all column tiles. Workgroups go
+    // round-robin to the 8 XCDs (id mod 8); each XCD owns a contiguous range of tile ids and
+    // its workgroups take consecutive ids in each round, so the tiles resident on one XCD at
+    // any time share A rows and B columns in its L2. With the tail split, the tiles of a
+    // last round that would be at most half full are left to the tail launch, which runs
+    // each of them as two 128-row halves (workgroup u: tile main_total + u/2, half u%2).
     int num_mt = args.meta[0];
     if (num_mt > args.max_tiles) num_mt = args.max_tiles;
     const int NT = args.n_tiles;
     const int total = num_mt * NT;
-    const int xcd = blockIdx.x & 7;
-    const int li = blockIdx.x >> 3;
-    const int per = total >> 3, rem = total & 7;
-    if (li >= per + (xcd < rem ? 1 : 0)) return;
-    const int v = xcd * per + (xcd < rem ? xcd : rem) + li;
+    int main_total = total;
+    if (args.split_round > 0) {
+        const int rem = total % args.split_round;
+        if (rem > 0 && 2 * rem <= args.split_round) main_total = total - rem;
+    }
+    int v, half = 0;
+    if (!args.tail) {
+        const int xcd = blockIdx.x & 7;
+        const int li = blockIdx.x >> 3;
+        const int per = main_total >> 3, rem = main_total & 7;
+        if (li >= per + (xcd < rem ? 1 : 0)) return;
+        v = xcd * per + (xcd < rem ? xcd : rem) + li;
+    } else {
+        const int u = blockIdx.x;
+        if (u >= 2 * (total - main_total)) return;
+        v = main_total + (u >> 1);
+        half = u & 1;
+    }
     const int grp = v / (kGroupM * NT);
     const int mt0 = grp * kGroupM;
     const int gm = min(kGroupM, num_mt - mt0);
@@ -185,7 +204,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
     const int mt = mt0 + vin % gm;
     const int nt = vin / gm;
     const int expert = args.tile_expert[mt];
-    const int row0 = args.tile_row0[mt];
+    const int row0 = args.tile_row0[mt] + half * BM;
     const int nks = args.K / kBK;              // >= 2
 
     // ---- A rows this lane fetches and reads scales for ----------------------------------
@@ -473,15 +492,55 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// Workgroups of a kernel the current device runs at once (CUs x workgroups per CU),
+// computed once per device; 0 if unknown.
+template <int BM, int WAVES_M, int WAVES_N, int MODE>
+int resident_workgroups() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (cached[dev] == 0) {
+        int cus = 0, per_cu = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                &per_cu, grouped_gemm_kernel<BM, WAVES_M, WAVES_N, MODE>, kThreads, 0) != hipSuccess)
+            return 0;
+        cached[dev] = cus * (per_cu > 0 ? per_cu : 1);
+    }
+    return cached[dev];
+}
+
 // Row-tile classes (4 waves each): 256 rows as 2x2 waves of 128x128, 128 rows as 2x2
-// waves of 64x128, 64 rows as 1x4 waves of 64x64.
+// waves of 64x128, 64 rows as 1x4 waves of 64x64. The 256-row class leaves a last round
+// that would be at most half full to a 128-row launch over tile halves (the tile count
+// is known only on the device, so that launch always goes out and finds its share).
 template <int MODE>
 hipError_t launch_mode(int block_m, const GemmArgs& a, hipStream_t stream) {
     if (a.max_tiles == 0 || a.n_tiles == 0) return hipSuccess;
     switch (block_m) {
-        case 256: return launch_cfg<256, 2, 2, MODE>(a, stream);
-        case 128: return launch_cfg<128, 2, 2, MODE>(a, stream);
-        case 64: return launch_cfg<64, 1, 4, MODE>(a, stream);
+        case 256: {
+            GemmArgs m = a;
+            m.split_round = resident_workgroups<256, 2, 2, MODE>();
+            m.tail = 0;
+            hipError_t e = launch_cfg<256, 2, 2, MODE>(m, stream);
+            if (e != hipSuccess || m.split_round == 0) return e;
+            GemmArgs t = m;
+            t.tail = 1;
+            grouped_gemm_kernel<128, 2, 2, MODE><<<(unsigned)m.split_round, kThreads, 0, stream>>>(t);
+            return hipGetLastError();
+        }
+        case 128: {
+            GemmArgs m = a;
+            m.split_round = 0;
+            m.tail = 0;
+            return launch_cfg<128, 2, 2, MODE>(m, stream);
+        }
+        case 64: {
+            GemmArgs m = a;
+            m.split_round = 0;
+            m.tail = 0;
+            return launch_cfg<64, 1, 4, MODE>(m, stream);
+        }
         default: return hipErrorInvalidValue;
     }
 }

@@ -65,6 +65,11 @@ struct GemmArgs {
     const int32_t* tile_row0;
     int n_tiles;               // column tiles per M tile
     int max_tiles;
+    // Tail split (256-row tiles only): when the last round of tiles (split_round workgroups
+    // run at once) is at most half full, its tiles are left to a second launch that runs
+    // each as two 128-row halves (tail = 1). 0 disables it.
+    int split_round;
+    int tail;
     // B operand: packed weights
     const uint8_t* b;
     const uint32_t* b_sf;
