@@ -47,8 +47,11 @@ constexpr int kGroupM = 4;
 constexpr int kThreads = 256;
 constexpr int kStages = 3;
 // Word 3 of a raw buffer descriptor on gfx950 (32-bit data format, no swizzle); with a zero
-// stride and a record count of 2^31-1 bytes, offsets are plain byte offsets.
+// stride, offsets are plain byte offsets, range-checked against the record count.
 constexpr int kRsrcWord3 = 0x00020000;
+// Record count of a raw buffer descriptor spanning the whole 32-bit offset range (every
+// A, h8 and weight offset stays below 2^32 under the accepted shapes).
+constexpr int kAllRecords = -1;   // 0xFFFFFFFF
 
 template <int N>
 struct IntC {
@@ -87,8 +90,8 @@ __device__ inline int requant_scale_byte(float amax) {
 // Largest of four non-negative floats over the 16 lanes of a DPP row (lanes 16r .. 16r+15),
 // in every lane, for four rows at once: swap neighbours, swap pairs, mirror each half row,
 // mirror the row. The values are compared as their bit patterns (non-negative floats order
-// like their bits), which needs no NaN canonicalisation; the four independent chains fill
-// each other's DPP wait states.
+// like their bits), which needs no NaN canonicalisation and lets each step be one DPP max;
+// the four independent chains fill each other's DPP wait states.
 __device__ inline void row16_max4(uint32_t (&m)[4]) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) m[r] = max(m[r], (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m[r], 0xB1, 0xF, 0xF, false));
@@ -244,12 +247,12 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
         if (MODE == 1) return fn < FN / 2 ? wn * (FN / 2) + fn : 8 + wn * (FN / 2) + (fn - FN / 2);
         return wn * FN + fn;
     };
-    const __amdgpu_buffer_rsrc_t rs_a = __builtin_amdgcn_make_buffer_rsrc((void*)args.a, 0, 0x7fffffff, kRsrcWord3);
-    const __amdgpu_buffer_rsrc_t rs_asf = __builtin_amdgcn_make_buffer_rsrc((void*)args.a_sf, 0, 0x7fffffff, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rs_a = __builtin_amdgcn_make_buffer_rsrc((void*)args.a, 0, kAllRecords, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rs_asf = __builtin_amdgcn_make_buffer_rsrc((void*)args.a_sf, 0, kAllRecords, kRsrcWord3);
     const __amdgpu_buffer_rsrc_t rs_b = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(args.b + (size_t)expert * args.b_expert + (size_t)nt * args.b_ntile), 0, 0x7fffffff, kRsrcWord3);
+        (void*)(args.b + (size_t)expert * args.b_expert + (size_t)nt * args.b_ntile), 0, kAllRecords, kRsrcWord3);
     const __amdgpu_buffer_rsrc_t rs_bsf = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(args.b_sf + (size_t)expert * args.bs_expert + (size_t)nt * args.bs_ntile), 0, 0x7fffffff, kRsrcWord3);
+        (void*)(args.b_sf + (size_t)expert * args.bs_expert + (size_t)nt * args.bs_ntile), 0, kAllRecords, kRsrcWord3);
     const uint32_t b_voff = (uint32_t)(wave * B_DMA * 1024 + lane * 16);
     const uint32_t bs_voff = (uint32_t)(lane * 4);
 
@@ -392,19 +395,23 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
             // stored as one word per lane and row.
             constexpr int FQ = FN / 2;
             const int l = lane & 15;
-            uint32_t* red = reinterpret_cast<uint32_t*>(ep);              // [WAVES_N][BM] |h| bits
+            uint32_t* red = reinterpret_cast<uint32_t*>(ep);              // [WAVES_N][BM] max |h| bits
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm) {
                 uint32_t m[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    m[r] = 0u;
+                    float h[FQ];
 #pragma unroll
                     for (int q = 0; q < FQ; ++q) {
-                        const float h = swiglu(acc[fm][q][r], acc[fm][q + FQ][r]);
-                        acc[fm][q][r] = h;                 // h replaces the gate sum
-                        m[r] = max(m[r], __float_as_uint(h) & 0x7fffffffu);
+                        h[q] = swiglu(acc[fm][q][r], acc[fm][q + FQ][r]);
+                        acc[fm][q][r] = h[q];              // h replaces the gate sum
                     }
+                    // the lane's largest |h| (abs is a free input modifier), then as bits
+                    if constexpr (FQ == 4)
+                        m[r] = __float_as_uint(fmaxf(fmaxf(fabsf(h[0]), fabsf(h[1])), fmaxf(fabsf(h[2]), fabsf(h[3]))));
+                    else
+                        m[r] = __float_as_uint(fmaxf(fabsf(h[0]), fabsf(h[1])));
                 }
                 row16_max4(m);
                 if (l == 0) {
@@ -413,9 +420,14 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
                 }
             }
             wait_lds_barrier();
+            // codes and scale bytes go out through buffer stores: a per-lane offset of the
+            // lane's first row and columns, plus a uniform offset of the row (row0 + fm*16 + r)
             const int fw = wn * FQ;                                      // first gate fragment
             const int col0 = 64 * (fw >> 2) + 4 * l + (fw & 3);
-            uint8_t* hbase = args.h8 + (size_t)row0 * args.h_stride + nt * 128 + col0;
+            const __amdgpu_buffer_rsrc_t rs_h8 = __builtin_amdgcn_make_buffer_rsrc(args.h8, 0, kAllRecords, kRsrcWord3);
+            const __amdgpu_buffer_rsrc_t rs_hsf = __builtin_amdgcn_make_buffer_rsrc(args.h_sf, 0, kAllRecords, kRsrcWord3);
+            const uint32_t h_lane = (uint32_t)((wm * WM + 4 * g) * args.h_stride + col0);
+            const uint32_t sf_lane = (uint32_t)((wm * WM + 4 * g) * args.h_sf_stride);
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm) {
 #pragma unroll
@@ -426,16 +438,19 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
                     for (int w = 1; w < WAVES_N; ++w) mb = max(mb, red[w * BM + rt]);
                     const int byte = requant_scale_byte(__uint_as_float(mb));
                     const float mul = __uint_as_float((uint32_t)(254 - byte) << 23);  // 2^-(byte-127)
-                    uint8_t* dst = hbase + (size_t)rt * args.h_stride;
+                    const uint32_t row_u = (uint32_t)(row0 + fm * 16 + r);
                     int pk = __builtin_amdgcn_cvt_pk_fp8_f32(acc[fm][0][r] * mul, acc[fm][1][r] * mul, 0, false);
                     if constexpr (FQ == 4) {
                         pk = __builtin_amdgcn_cvt_pk_fp8_f32(acc[fm][2][r] * mul, acc[fm][3][r] * mul, pk, true);
-                        *reinterpret_cast<uint32_t*>(dst) = (uint32_t)pk;
+                        __builtin_amdgcn_raw_buffer_store_b32((uint32_t)pk, rs_h8, h_lane,
+                                                              row_u * (uint32_t)args.h_stride + nt * 128, 0);
                     } else {
-                        *reinterpret_cast<uint16_t*>(dst) = (uint16_t)pk;
+                        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)pk, rs_h8, h_lane,
+                                                              row_u * (uint32_t)args.h_stride + nt * 128, 0);
                     }
                     if (wn == 0 && l == 0)
-                        args.h_sf[(size_t)(row0 + rt) * args.h_sf_stride + nt] = (uint8_t)byte;
+                        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)byte, rs_hsf, sf_lane,
+                                                             row_u * (uint32_t)args.h_sf_stride + nt, 0);
                 }
             }
         } else {

@@ -200,3 +200,23 @@ def test_weight_and_scale_doubling():
     assert rows == int(run_u.routing()["offsets"][-1])
     assert np.array_equal(h8a, h8b)
     assert np.array_equal(sfb.astype(np.int32), sfa.astype(np.int32) + 1)
+
+
+def test_offsets_beyond_2gib():
+    """x holds more than 2^31 bytes (T = 300000, H = 7168), so the rows of the last tokens
+    sit at byte offsets past 2^31 in the GEMM's A loads; their outputs must still match."""
+    cfg = MoEConfig("big", T=300000, E=4, k=1, H=7168, I=256)
+    print(f"[edge] offsets past 2 GiB {cfg}", flush=True)
+    inp = make_inputs(cfg, seed=17, device="cuda")
+    assert inp.x_fp8.numel() > 2**31
+    run = Run(inp)
+    y = run.forward(poison=False)
+    idx = inp.topk_idx.cpu().numpy()
+    got = run.routing()
+    check_routing(got, idx, cfg.E)
+    toks = [0, 1, 299593, 299594, 299998, 299999]      # rows below and above byte 2^31
+    assert 299594 * cfg.H >= 2**31
+    host = _host(inp)
+    ref = oracle.forward_inputs(host, tokens=toks, keep_bounds=True)
+    check_intermediates(run, ref, got["inv"])
+    check_y(y, ref, tokens=toks)
