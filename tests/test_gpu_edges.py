@@ -220,3 +220,28 @@ def test_offsets_beyond_2gib():
     ref = oracle.forward_inputs(host, tokens=toks, keep_bounds=True)
     check_intermediates(run, ref, got["inv"])
     check_y(y, ref, tokens=toks)
+
+
+def test_two_streams_two_workspaces():
+    """Calls on different streams with different workspaces are independent: two forwards
+    launched back to back on two streams give the bytes each gives alone."""
+    cfg_a = MoEConfig("sa", T=900, E=6, k=2, H=512, I=384)
+    cfg_b = MoEConfig("sb", T=700, E=3, k=3, H=256, I=640)
+    print(f"[edge] two streams {cfg_a} {cfg_b}", flush=True)
+    ia = make_inputs(cfg_a, seed=31, device="cuda")
+    ib = make_inputs(cfg_b, seed=32, device="cuda")
+    ra, rb = Run(ia), Run(ib)
+    ya = ra.forward().copy()
+    yb = rb.forward().copy()
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    for _ in range(3):
+        ra.y.fill_(0); rb.y.fill_(0)
+        torch.cuda.synchronize()
+        moe.moe_forward(ra.y, ia.x_fp8, ia.x_sf, ia.topk_idx, ia.topk_weights, cfg_a.T, ra.shape,
+                        ra.packed, ra.ws, stream=sa)
+        moe.moe_forward(rb.y, ib.x_fp8, ib.x_sf, ib.topk_idx, ib.topk_weights, cfg_b.T, rb.shape,
+                        rb.packed, rb.ws, stream=sb)
+        torch.cuda.synchronize()
+        assert np.array_equal(ra.y[: cfg_a.T].cpu().numpy().view(np.uint16), ya)
+        assert np.array_equal(rb.y[: cfg_b.T].cpu().numpy().view(np.uint16), yb)
