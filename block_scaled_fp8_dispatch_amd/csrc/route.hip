@@ -7,7 +7,9 @@
 // together with each group block-aligned. Here only indices move: the GEMM gathers the
 // activation rows through `perm`.
 //
-// Three launches, all deterministic:
+// Up to kFusedMaxSlots slots, one launch of one workgroup does all of it (histogram,
+// scan, then the stable scatter in rounds of 1024 slots): small batches are bound by
+// launch latency, not work. Larger inputs take three launches, all deterministic:
 //   count   one workgroup per chunk of kRouteChunk slots: per-expert histogram of the
 //           chunk (LDS integer atomics; the count does not depend on their order) and
 //           the chunk's number of invalid ids
@@ -22,6 +24,125 @@ namespace {
 
 constexpr int kMaxE = MOE_MAX_EXPERTS;
 constexpr int kSlotsPerThread = kRouteChunk / kRouteThreads;
+constexpr int kFusedThreads = 1024;
+constexpr int kFusedMaxSlots = 4096;   // measured: one workgroup beats three launches up to here
+
+// Exclusive scan of `v` over the 1024 threads of a workgroup (thread order); the total
+// goes to *total. warp_sums: 16 ints of LDS.
+__device__ inline int block_exclusive_scan_1024(int v, int* warp_sums, int* total) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    int incl = v;
+    for (int d = 1; d < 64; d <<= 1) {
+        const int t = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += t;
+    }
+    if (lane == 63) warp_sums[wave] = incl;
+    __syncthreads();
+    int wave_base = 0, all = 0;
+    for (int w = 0; w < 16; ++w) {
+        if (w < wave) wave_base += warp_sums[w];
+        all += warp_sums[w];
+    }
+    *total = all;
+    return wave_base + incl - v;
+}
+
+// Stable rank of slot s among the slots of this round with the same expert id, for one
+// wave: lanes holding the same id match on every bit of it (ballots).
+__device__ inline void wave_match(int e, bool ok, int nbits, int lane, int& rank_w, int& cnt) {
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    uint64_t peers = __ballot(ok);
+    for (int b = 0; b < nbits; ++b) {
+        const bool bit = (e >> b) & 1;
+        const uint64_t bal = __ballot(bit);
+        peers &= bit ? bal : ~bal;
+    }
+    rank_w = __popcll(peers & lt_mask);
+    cnt = __popcll(peers);
+}
+
+__global__ __launch_bounds__(kFusedThreads) void route_fused_kernel(
+    const int32_t* __restrict__ idx, int num_slots, int E, int nbits, int block_m,
+    int32_t* __restrict__ meta, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ perm, int32_t* __restrict__ inv, int32_t* __restrict__ tile_expert,
+    int32_t* __restrict__ tile_row0, int max_tiles) {
+    __shared__ int hist[kMaxE];                          // then: next row of each expert
+    __shared__ int wave_cnt[kFusedThreads / 64][kMaxE];
+    __shared__ int warp_sums[16];
+    __shared__ int invalid;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    for (int e = tid; e < E; e += kFusedThreads) {
+        hist[e] = 0;
+        for (int w = 0; w < kFusedThreads / 64; ++w) wave_cnt[w][e] = 0;
+    }
+    if (tid == 0) invalid = 0;
+    __syncthreads();
+    // histogram and invalid ids
+    int my_invalid = 0;
+    for (int s = tid; s < num_slots; s += kFusedThreads) {
+        const int e = idx[s];
+        if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
+        else if (e != -1) ++my_invalid;
+    }
+    if (my_invalid) atomicAdd(&invalid, my_invalid);
+    __syncthreads();
+    // padded exclusive scan over experts (thread e owns expert e), tile list, padding rows
+    const int c = tid < E ? hist[tid] : 0;
+    const int pad = (c + block_m - 1) / block_m * block_m;
+    int total = 0;
+    const int excl = block_exclusive_scan_1024(pad, warp_sums, &total);
+    if (tid < E) {
+        counts[tid] = c;
+        offsets[tid] = excl;
+        if (tid == E - 1) offsets[E] = excl + pad;
+        for (int r = excl + c; r < excl + pad; ++r) perm[r] = -1;
+        for (int r = excl; r < excl + pad; r += block_m) {
+            const int t = r / block_m;
+            if (t < max_tiles) {
+                tile_expert[t] = tid;
+                tile_row0[t] = r;
+            }
+        }
+        hist[tid] = excl;                                // next row of expert tid
+    }
+    if (tid == 0) {
+        meta[0] = total / block_m;
+        meta[1] = invalid;
+        meta[2] = block_m;
+    }
+    __syncthreads();
+    // stable scatter, 1024 slots per round in slot order
+    for (int s0 = 0; s0 < num_slots; s0 += kFusedThreads) {
+        const int s = s0 + tid;
+        const bool in_range = s < num_slots;
+        const int e = in_range ? idx[s] : -1;
+        const bool ok = e >= 0 && e < E;
+        int rank_w, cnt;
+        wave_match(e, ok, nbits, lane, rank_w, cnt);
+        if (ok && rank_w == cnt - 1) wave_cnt[wave][e] = cnt;
+        __syncthreads();
+        if (ok) {
+            int pos = hist[e] + rank_w;
+            for (int w = 0; w < wave; ++w) pos += wave_cnt[w][e];
+            perm[pos] = s;
+            inv[s] = pos;
+        } else if (in_range) {
+            inv[s] = -1;
+        }
+        __syncthreads();
+        for (int x = tid; x < E; x += kFusedThreads) {
+            int add = 0;
+            for (int w = 0; w < kFusedThreads / 64; ++w) {
+                add += wave_cnt[w][x];
+                wave_cnt[w][x] = 0;
+            }
+            hist[x] += add;
+        }
+        __syncthreads();
+    }
+}
 
 __global__ __launch_bounds__(kRouteThreads) void route_count_kernel(
     const int32_t* __restrict__ idx, int num_slots, int E, int32_t* __restrict__ blk_counts,
@@ -171,6 +292,12 @@ hipError_t launch_route(const int32_t* topk_idx, int num_slots, int E, int block
     int32_t* blk_invalid = blk_counts + (size_t)nblk * E;
     int nbits = 1;
     while ((1 << nbits) < E) ++nbits;
+    if (num_slots <= kFusedMaxSlots) {
+        route_fused_kernel<<<1, kFusedThreads, 0, stream>>>(topk_idx, num_slots, E, nbits, block_m, meta,
+                                                           counts, offsets, perm, inv, tile_expert,
+                                                           tile_row0, max_tiles);
+        return hipGetLastError();
+    }
     route_count_kernel<<<nblk, kRouteThreads, 0, stream>>>(topk_idx, num_slots, E, blk_counts,
                                                             blk_invalid);
     route_scan_kernel<<<1, 1024, 0, stream>>>(blk_counts, blk_invalid, nblk, E, block_m, meta,
