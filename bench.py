@@ -92,7 +92,7 @@ def cpu_baseline(inp_cpu: dict, cfg, n_tokens: int):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); the multi-GPU "
+        print(f"bench.py: this benchmark runs on one GPU only (got --gpus {args.gpus}); the multi-GPU "
               "expert-parallel exchange is not part of it", file=sys.stderr)
         sys.exit(2)
     import numpy as np
@@ -188,7 +188,7 @@ def main():
         "stage_ms": {"dispatch": round(float(st_ms[0]), 4), "linear1": round(float(st_ms[1]), 4),
                      "linear2": round(float(st_ms[2]), 4), "combine": round(float(st_ms[3]), 4)},
         "wall_s_timed": round(wall, 3),
-        "roofline": {"bound": "mfma", "kernel": "Linear1 grouped GEMM (+SwiGLU/requant epilogue)",
+        "roofline": {"bound": "mfma", "kernel": "Linear1 grouped GEMM with SwiGLU/requant epilogue (main + tail launch)",
                      "achieved": round(l1_tflops, 2), "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(l1_tflops / PEAK_TFLOPS, 4), "traffic": traffic},
         "cpu_baseline": None,

@@ -57,8 +57,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     if _lib is not None:
         return _lib
     if not os.path.exists(path):
-        raise ImportError(f"{path} not found: build it with `python -m block_scaled_fp8_dispatch_amd.build` "
-                          "(or __graft_entry__.build()); the MoE forward has no other implementation")
+        raise ImportError(f"{path} not found: build it with `python -m block_scaled_fp8_dispatch_amd.build`; "
+                          "the MoE forward has no other implementation")
     lib = ctypes.CDLL(path)
     P, S, I32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
     shp = ctypes.POINTER(moe_shape_t)

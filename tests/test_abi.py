@@ -22,7 +22,7 @@ def _header_functions():
 @pytest.fixture(scope="module")
 def lib():
     if not os.path.exists(moe.LIB_PATH):
-        pytest.fail("libmoe.so is not built (run __graft_entry__.build())")
+        pytest.fail("libmoe.so is not built (run python -m block_scaled_fp8_dispatch_amd.build)")
     return moe.load_library()
 
 
