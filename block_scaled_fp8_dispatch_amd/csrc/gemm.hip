@@ -216,18 +216,24 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
     // 8*(w*A_DMA + j) .. +7 of the A tile; lane l lands at row + l/8, physical 16-byte chunk
     // l%8, which holds logical chunk (l%8) ^ (row%8).
     const int a_chunk = (lane & 7) ^ (lane >> 3);
+    // Linear2 reads h8 in its blocked layout: row r of the tile at K step ks sits at
+    // (tile block + ks) * hblk * 128 + (row in block) * 128; the per-step part goes in the
+    // uniform offset. Linear1 reads x rows (row-major, gathered through perm).
+    const int NKB = args.K / kBK;
+    const uint32_t a_kstep = MODE == 2 ? (uint32_t)args.hblk * kBK : (uint32_t)kBK;
     uint32_t a_off[A_DMA];
 #pragma unroll
     for (int j = 0; j < A_DMA; ++j) {
         const int r = 8 * (wave * A_DMA + j) + (lane >> 3);
-        uint32_t row;
         if (MODE == 1) {
             const int slot = args.perm[row0 + r];
-            row = slot >= 0 ? (uint32_t)(slot / args.topk) : 0u;
+            const uint32_t row = slot >= 0 ? (uint32_t)(slot / args.topk) : 0u;
+            a_off[j] = row * (uint32_t)args.a_stride + a_chunk * 16;
         } else {
-            row = (uint32_t)(row0 + r);
+            const uint32_t blk_row = (uint32_t)(row0 / args.hblk) * (uint32_t)NKB * (uint32_t)args.hblk +
+                                     (uint32_t)(row0 % args.hblk + r);
+            a_off[j] = blk_row * kBK + a_chunk * 16;
         }
-        a_off[j] = row * (uint32_t)args.a_stride + a_chunk * 16;
     }
     uint32_t sa_off[FM];
 #pragma unroll
@@ -262,7 +268,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
         uint8_t* As = smem + slot * STAGE_BYTES;
         if (j < A_DMA) {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_a, MOE_LPTR(As + (wave * A_DMA + j) * 1024), 16,
-                                                     a_off[j], ks * kBK, 0, 0);
+                                                     a_off[j], ks * a_kstep, 0, 0);
         } else {
             const int jj = j - A_DMA;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_b, MOE_LPTR(As + A_BYTES + (wave * B_DMA + jj) * 1024),
@@ -426,7 +432,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
             const int col0 = 64 * (fw >> 2) + 4 * l + (fw & 3);
             const __amdgpu_buffer_rsrc_t rs_h8 = __builtin_amdgcn_make_buffer_rsrc(args.h8, 0, kAllRecords, kRsrcWord3);
             const __amdgpu_buffer_rsrc_t rs_hsf = __builtin_amdgcn_make_buffer_rsrc(args.h_sf, 0, kAllRecords, kRsrcWord3);
-            const uint32_t h_lane = (uint32_t)((wm * WM + 4 * g) * args.h_stride + col0);
+            // h8 block (row tile, K block nt of Linear2): hblk rows of 128 bytes
+            const uint32_t h_blk = ((uint32_t)(row0 / args.hblk) * (uint32_t)(args.h_stride / 128) + nt) *
+                                   (uint32_t)args.hblk * 128u + (uint32_t)(row0 % args.hblk) * 128u;
+            const uint32_t h_lane = (uint32_t)((wm * WM + 4 * g) * 128 + col0);
             const uint32_t sf_lane = (uint32_t)((wm * WM + 4 * g) * args.h_sf_stride);
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm) {
@@ -443,10 +452,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
                     if constexpr (FQ == 4) {
                         pk = __builtin_amdgcn_cvt_pk_fp8_f32(acc[fm][2][r] * mul, acc[fm][3][r] * mul, pk, true);
                         __builtin_amdgcn_raw_buffer_store_b32((uint32_t)pk, rs_h8, h_lane,
-                                                              row_u * (uint32_t)args.h_stride + nt * 128, 0);
+                                                              h_blk + (uint32_t)(fm * 16 + r) * 128u, 0);
                     } else {
                         __builtin_amdgcn_raw_buffer_store_b16((uint16_t)pk, rs_h8, h_lane,
-                                                              row_u * (uint32_t)args.h_stride + nt * 128, 0);
+                                                              h_blk + (uint32_t)(fm * 16 + r) * 128u, 0);
                     }
                     if (wn == 0 && l == 0)
                         __builtin_amdgcn_raw_buffer_store_b8((uint8_t)byte, rs_hsf, sf_lane,

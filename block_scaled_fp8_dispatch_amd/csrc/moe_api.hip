@@ -204,6 +204,7 @@ static int forward_impl(uint16_t* y_bf16, const uint8_t* x_fp8, const uint8_t* x
     a1.h8 = ws + W.pub.h8;
     a1.h_sf = ws + W.pub.h_sf;
     a1.h_stride = I;
+    a1.hblk = BM;
     a1.h_sf_stride = (int)W.pub.h_sf_stride;
     if (launch_linear1(BM, a1, stream) != hipSuccess) return MOE_ERR_HIP;
     if (mark(2) != hipSuccess) return MOE_ERR_HIP;

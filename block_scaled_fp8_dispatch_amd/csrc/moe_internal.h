@@ -75,6 +75,9 @@ struct GemmArgs {
     const uint32_t* b_sf;
     size_t b_expert, b_ntile;        // bytes
     size_t bs_expert, bs_ntile;      // 32-bit words
+    // h8 is stored in blocks of hblk rows x 128 columns, [P_pad/hblk][I/128][hblk][128]: the
+    // block a Linear1 tile writes is the A block one Linear2 K step reads, contiguous
+    int hblk;
     // Linear1 outputs
     uint8_t* h8;
     uint8_t* h_sf;

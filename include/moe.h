@@ -133,7 +133,10 @@ typedef struct {
     size_t inv;             /* i32[T*k]    row of each slot, -1 if skipped */
     size_t tile_expert;     /* i32[max_tiles] */
     size_t tile_row0;       /* i32[max_tiles] */
-    size_t h8;              /* u8 [P_pad, I]            FP8 intermediate */
+    size_t h8;              /* u8 FP8 intermediate in blocks of block_m rows x 128 columns,
+                               [P_pad/block_m][I/128][block_m][128]: padded row p, column c
+                               at ((p/block_m)*(I/128) + c/128)*block_m*128 + (p%block_m)*128
+                               + c%128 */
     size_t h_sf;            /* u8 [P_pad, 4*ceil(I/512)] its UE8M0 scales */
     size_t h_sf_stride;     /* bytes per h_sf row */
     size_t stage;           /* u16[T*k, H]  weighted bf16 Linear2 rows, by slot */

@@ -26,9 +26,11 @@ class Run:
         moe.moe_prepare_weights(self.shape, inp.w1, inp.w1_sf, inp.w2, inp.w2_sf, self.packed)
         self.ws = torch.empty(moe.moe_workspace_bytes(self.shape), dtype=torch.uint8, device=device)
         self.y = torch.empty(max(self.T, 1), cfg.H, dtype=torch.int16, device=device)
+        self.last_T = self.T
 
     def forward(self, T=None, poison=True):
         T = self.T if T is None else T
+        self.last_T = T
         if poison:
             self.ws.fill_(0xFF)
             self.y.fill_(0x7FBF)
@@ -57,14 +59,20 @@ class Run:
             tile_expert=self.ws_i32(L["tile_expert"], ntiles),
             tile_row0=self.ws_i32(L["tile_row0"], ntiles), num_invalid=meta[1])
 
-    def intermediates(self, rows):
-        """h8 codes [len(rows), I] and h_sf bytes [len(rows), I/128] of the given perm rows."""
-        L = self.layout()
+    def intermediates(self, rows, T=None):
+        """h8 codes [len(rows), I] and h_sf bytes [len(rows), I/128] of the given padded rows
+        (h8 is stored in blocks of block_m rows x 128 columns; h_sf row-major)."""
+        L = self.layout(self.last_T if T is None else T)
         I = self.shape.intermediate
+        hb = L["block_m"]
         sfs = L["h_sf_stride"]
-        n = int(np.max(rows)) + 1
-        rt = torch.as_tensor(np.asarray(rows, dtype=np.int64), device=self.ws.device)
-        h8 = self.ws[L["h8"]: L["h8"] + n * I].view(n, I)[rt].cpu().numpy()
+        rows = np.asarray(rows, dtype=np.int64)
+        n = int(rows.max()) + 1
+        nblk = (n + hb - 1) // hb
+        h8 = self.ws[L["h8"]: L["h8"] + nblk * hb * I].view(nblk, I // 128, hb, 128)
+        h8 = h8.permute(0, 2, 1, 3).reshape(nblk * hb, I)
+        rt = torch.as_tensor(rows, device=self.ws.device)
+        h8 = h8[rt].cpu().numpy()
         hs = self.ws[L["h_sf"]: L["h_sf"] + n * sfs].view(n, sfs)[rt][:, : I // 128].cpu().numpy()
         return h8, hs
 
