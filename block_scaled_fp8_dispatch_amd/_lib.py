@@ -45,7 +45,8 @@ class moe_layout_t(ctypes.Structure):
                 ("inv", ctypes.c_size_t), ("tile_expert", ctypes.c_size_t),
                 ("tile_row0", ctypes.c_size_t), ("h8", ctypes.c_size_t),
                 ("h_sf", ctypes.c_size_t), ("h_sf_stride", ctypes.c_size_t),
-                ("stage", ctypes.c_size_t), ("total", ctypes.c_size_t)]
+                ("stage", ctypes.c_size_t), ("xg", ctypes.c_size_t),
+                ("xg_sf", ctypes.c_size_t), ("total", ctypes.c_size_t)]
 
 
 _lib: Optional[ctypes.CDLL] = None

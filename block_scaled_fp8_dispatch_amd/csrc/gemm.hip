@@ -2,8 +2,8 @@
 // (v_mfma_scale_f32_16x16x128_f8f6f4: A e4m3, B E2M1, one UE8M0 scale per lane per
 // instruction, FP32 accumulation).
 //
-//   Linear1 (chenxutan.com/d/1930 section 3.1 step 2): rows of x gathered through the
-//     dispatch permutation x packed W1 of the row tile's expert; the epilogue applies
+//   Linear1 (chenxutan.com/d/1930 section 3.1 step 2): the dispatched rows of x (copied
+//     into expert order by the dispatch) x packed W1 of the row tile's expert; the epilogue applies
 //     SwiGLU (step 3) and requantises h to e4m3 with one UE8M0 scale per 1x128 block
 //     (section 11.1's per-block amax scaling, rounded up to a power of two).
 //   Linear2 (step 4): rows of h8 x packed W2; the epilogue multiplies each row by its
@@ -216,37 +216,35 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
     // 8*(w*A_DMA + j) .. +7 of the A tile; lane l lands at row + l/8, physical 16-byte chunk
     // l%8, which holds logical chunk (l%8) ^ (row%8).
     const int a_chunk = (lane & 7) ^ (lane >> 3);
-    // Linear2 reads h8 in its blocked layout: row r of the tile at K step ks sits at
-    // (tile block + ks) * hblk * 128 + (row in block) * 128; the per-step part goes in the
-    // uniform offset. Linear1 reads x rows (row-major, gathered through perm).
+    // A blocked (h8 for Linear2, the dispatched x for Linear1): row r of the tile at K step
+    // ks sits at (tile block + ks) * hblk * 128 + (row in block) * 128, the per-step part in
+    // the uniform offset, and its scale row is the padded row. Otherwise (Linear1 without a
+    // dispatch copy) A is x itself, row-major, its rows the tokens perm names (padding rows
+    // read token 0 and are never stored).
+    const bool blocked = MODE == 2 || args.a_blocked != 0;
     const int NKB = args.K / kBK;
-    const uint32_t a_kstep = MODE == 2 ? (uint32_t)args.hblk * kBK : (uint32_t)kBK;
+    const uint32_t a_kstep = blocked ? (uint32_t)args.hblk * kBK : (uint32_t)kBK;
+    auto src_row = [&](int r) __attribute__((always_inline)) -> uint32_t {
+        const int slot = args.perm[row0 + r];
+        return slot >= 0 ? (uint32_t)(slot / args.topk) : 0u;
+    };
     uint32_t a_off[A_DMA];
 #pragma unroll
     for (int j = 0; j < A_DMA; ++j) {
         const int r = 8 * (wave * A_DMA + j) + (lane >> 3);
-        if (MODE == 1) {
-            const int slot = args.perm[row0 + r];
-            const uint32_t row = slot >= 0 ? (uint32_t)(slot / args.topk) : 0u;
-            a_off[j] = row * (uint32_t)args.a_stride + a_chunk * 16;
-        } else {
+        if (blocked) {
             const uint32_t blk_row = (uint32_t)(row0 / args.hblk) * (uint32_t)NKB * (uint32_t)args.hblk +
                                      (uint32_t)(row0 % args.hblk + r);
             a_off[j] = blk_row * kBK + a_chunk * 16;
+        } else {
+            a_off[j] = src_row(r) * (uint32_t)args.a_stride + a_chunk * 16;
         }
     }
     uint32_t sa_off[FM];
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
         const int r = wm * WM + fm * 16 + (lane & 15);
-        uint32_t row;
-        if (MODE == 1) {
-            const int slot = args.perm[row0 + r];
-            row = slot >= 0 ? (uint32_t)(slot / args.topk) : 0u;
-        } else {
-            row = (uint32_t)(row0 + r);
-        }
-        sa_off[fm] = row * (uint32_t)args.a_sf_stride;
+        sa_off[fm] = (blocked ? (uint32_t)(row0 + r) : src_row(r)) * (uint32_t)args.a_sf_stride;
     }
     // B fragment index of the wave's n-th fragment
     auto bfrag = [&](int fn) __attribute__((always_inline)) -> int {

@@ -53,12 +53,14 @@ hipError_t launch_pack(const moe_shape_t& s, const PackedLayout& L,
 // Grouped GEMMs (gemm.hip)
 struct GemmArgs {
     // A operand: rows of FP8 codes with per-1x128 UE8M0 scales
-    const uint8_t* a;          // x_fp8 (Linear1, gathered through perm) or h8 (Linear2)
+    const uint8_t* a;          // A rows: blocked (h8, or the dispatched x) or x itself
+    int a_blocked;             // 1: A blocked like h8, scale rows = padded rows;
+                               // 0 (Linear1 only): rows of x gathered through perm
     const uint8_t* a_sf;
     int a_stride;              // bytes per A row (= K)
     int a_sf_stride;           // bytes per A scale row
     int K;                     // reduction length (multiple of 128)
-    int topk;                  // Linear1: slot -> token = slot / topk
+    int topk;                  // a_blocked == 0: slot -> token = slot / topk
     const int32_t* perm;
     const int32_t* meta;       // meta[0] = number of M tiles in use
     const int32_t* tile_expert;
@@ -91,6 +93,12 @@ struct GemmArgs {
 
 hipError_t launch_linear1(int block_m, const GemmArgs& a, hipStream_t stream);
 hipError_t launch_linear2(int block_m, const GemmArgs& a, hipStream_t stream);
+
+// Dispatch copy (route.hip): the x row and scales of each padded row's token into the
+// blocked A layout of Linear1 (zero on padding rows)
+hipError_t launch_gather(const uint8_t* x, const uint8_t* x_sf, const int32_t* perm,
+                         const int32_t* meta, int k, int H, int sfs, int hblk, int max_rows,
+                         uint8_t* xg, uint8_t* xg_sf, hipStream_t stream);
 
 // Combine (combine.hip)
 hipError_t launch_combine(const uint16_t* stage, const int32_t* topk_idx, int T, int k, int E,

@@ -4,8 +4,9 @@
 // The explainer (chenxutan.com/d/1930 section 3.1, step 1) describes dispatch as moving
 // each token to its experts' regions; the contiguous-layout grouped GEMM
 // (juejin.cn/post/7631516744872673307, "MoE模型专属优化") keeps every expert's rows
-// together with each group block-aligned. Here only indices move: the GEMM gathers the
-// activation rows through `perm`.
+// together with each group block-aligned. After the routing, a copy moves each padded
+// row's activation row and scales into expert order, in the blocked layout the GEMM reads
+// (one contiguous 1 KB piece per load).
 //
 // Up to kFusedMaxSlots slots, one launch of one workgroup does all of it (histogram,
 // scan, then the stable scatter in rounds of 1024 slots): small batches are bound by
@@ -282,7 +283,54 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(
     }
 }
 
+// Dispatch copy: thread d writes bytes [16d, 16d+16) of the blocked buffer
+// [P_pad/hblk][H/128][hblk][128] (consecutive threads, consecutive bytes): padded row
+// p = blk*hblk + r, columns kb*128 + 16*c8 .. +15, from the x row of token perm[p]/k (zero
+// on padding rows). The first rows*sfs/4 threads also copy one 32-bit scale word each.
+__global__ __launch_bounds__(256) void gather_kernel(const uint8_t* __restrict__ x,
+                                                     const uint8_t* __restrict__ x_sf,
+                                                     const int32_t* __restrict__ perm,
+                                                     const int32_t* __restrict__ meta, int k, int H,
+                                                     int sfs, int hblk, int max_rows,
+                                                     uint8_t* __restrict__ xg,
+                                                     uint8_t* __restrict__ xg_sf) {
+    int rows = meta[0] * hblk;
+    if (rows > max_rows) rows = max_rows;
+    const size_t d = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
+    const int nkb = H / 128;
+    if (d < (size_t)rows * (H / 16)) {
+        const int c8 = (int)(d & 7);
+        const size_t q = d >> 3;
+        const int r = (int)(q % hblk);
+        const size_t q2 = q / hblk;
+        const int kb = (int)(q2 % nkb);
+        const int blk = (int)(q2 / nkb);
+        const int p = blk * hblk + r;
+        const int slot = perm[p];
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (slot >= 0) v = *reinterpret_cast<const uint4*>(x + (size_t)(slot / k) * H + kb * 128 + c8 * 16);
+        *reinterpret_cast<uint4*>(xg + d * 16) = v;
+    }
+    const int words = sfs / 4;
+    if (d < (size_t)rows * words) {
+        const int p = (int)(d / words), w = (int)(d % words);
+        const int slot = perm[p];
+        const uint32_t v = slot >= 0 ? reinterpret_cast<const uint32_t*>(x_sf + (size_t)(slot / k) * sfs)[w] : 0u;
+        reinterpret_cast<uint32_t*>(xg_sf + (size_t)p * sfs)[w] = v;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_gather(const uint8_t* x, const uint8_t* x_sf, const int32_t* perm,
+                         const int32_t* meta, int k, int H, int sfs, int hblk, int max_rows,
+                         uint8_t* xg, uint8_t* xg_sf, hipStream_t stream) {
+    const size_t n = (size_t)max_rows * (H / 16);
+    if (n == 0) return hipSuccess;
+    gather_kernel<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(x, x_sf, perm, meta, k, H, sfs, hblk,
+                                                                  max_rows, xg, xg_sf);
+    return hipGetLastError();
+}
 
 hipError_t launch_route(const int32_t* topk_idx, int num_slots, int E, int block_m,
                         int32_t* blk_counts, int32_t* meta, int32_t* counts, int32_t* offsets,

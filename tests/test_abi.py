@@ -60,7 +60,7 @@ def test_layout_is_consistent(lib):
     assert L["block_m"] == 256
     assert moe.moe_workspace_layout(s, 128)["block_m"] == 64
     offs = [L[k] for k in ("meta", "counts", "offsets", "perm", "inv", "tile_expert", "tile_row0",
-                           "h8", "h_sf", "stage")]
+                           "h8", "h_sf", "stage", "xg", "xg_sf")]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
     assert L["h_sf_stride"] == 4 * ((2048 + 511) // 512)
     with pytest.raises(moe.MoEError):
