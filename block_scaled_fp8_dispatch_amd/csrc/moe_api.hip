@@ -12,6 +12,10 @@ namespace {
 
 constexpr int kMaxBlockM = 256;
 constexpr int kMinBlockM = 64;
+// Largest top-k for which dispatch copies x into the blocked layout Linear1 reads. The copy
+// pays off when each token is copied at most twice: at T=8192, k=2 it makes Linear1 4-5 %
+// faster for 1 % of the forward; at k=8 it costs more than it saves.
+constexpr int kDispatchCopyMaxTopk = 2;
 
 bool shape_ok(const moe_shape_t* s) {
     if (!s) return false;
@@ -26,7 +30,8 @@ bool shape_ok(const moe_shape_t* s) {
     // 32-bit row offsets inside the GEMM kernels
     if ((uint64_t)s->max_tokens * (uint64_t)s->hidden >= (1ull << 32)) return false;
     if (ppad * (uint64_t)s->intermediate >= (1ull << 32)) return false;
-    if (ppad * (uint64_t)s->hidden >= (1ull << 32)) return false;
+    if (s->num_topk <= kDispatchCopyMaxTopk && ppad * (uint64_t)s->hidden >= (1ull << 32))
+        return false;
     return true;
 }
 
@@ -79,8 +84,9 @@ WsLayout ws_layout(const moe_shape_t& s) {
     w.pub.h_sf = take(ppad * sfs);
     w.pub.h_sf_stride = sfs;
     w.pub.stage = take(slots * H * sizeof(uint16_t));
-    w.pub.xg = take(ppad * H);
-    w.pub.xg_sf = take(ppad * 4 * ((H + 511) / 512));
+    const bool copy = s.num_topk <= kDispatchCopyMaxTopk;
+    w.pub.xg = take(copy ? ppad * H : 0);
+    w.pub.xg_sf = take(copy ? ppad * 4 * ((H + 511) / 512) : 0);
     w.pub.total = off;
     w.pub.max_tiles = (int32_t)max_tiles;
     w.max_pad_rows = (int)ppad;
@@ -177,11 +183,8 @@ static int forward_impl(uint16_t* y_bf16, const uint8_t* x_fp8, const uint8_t* x
                      i32(W.pub.offsets), perm, i32(W.pub.inv), tile_e, tile_r, W.pub.max_tiles,
                      stream) != hipSuccess)
         return MOE_ERR_HIP;
-    // The dispatch copy pays off when each token is copied at most twice: measured at
-    // T=8192, k=2 it makes Linear1 5 % faster for 1 % of the forward; at k=8 it costs more
-    // than it saves.
     const int xsfs = 4 * ((H + 511) / 512);
-    const bool dispatch_copy = k <= 2;
+    const bool dispatch_copy = k <= kDispatchCopyMaxTopk;
     if (dispatch_copy && launch_gather(x_fp8, x_sf, perm, meta, k, H, xsfs, BM, W.max_pad_rows,
                                        ws + W.pub.xg, ws + W.pub.xg_sf, stream) != hipSuccess)
         return MOE_ERR_HIP;

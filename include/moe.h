@@ -140,10 +140,11 @@ typedef struct {
     size_t h_sf;            /* u8 [P_pad, 4*ceil(I/512)] its UE8M0 scales */
     size_t h_sf_stride;     /* bytes per h_sf row */
     size_t stage;           /* u16[T*k, H]  weighted bf16 Linear2 rows, by slot */
-    size_t xg;              /* u8 the dispatched activations (written when num_topk <= 2):
-                               the x row of each padded row's token (zero on padding rows),
-                               blocked like h8 with H columns: [P_pad/block_m][H/128][block_m][128] */
-    size_t xg_sf;           /* u8 [P_pad, 4*ceil(H/512)] their UE8M0 scales */
+    size_t xg;              /* u8 the dispatched activations, only when num_topk <= 2 (zero
+                               bytes otherwise: xg == xg_sf == total): the x row of each padded
+                               row's token (zero on padding rows), blocked like h8 with H
+                               columns: [P_pad/block_m][H/128][block_m][128] */
+    size_t xg_sf;           /* u8 [P_pad, 4*ceil(H/512)] their UE8M0 scales (num_topk <= 2) */
     size_t total;           /* bytes used */
 } moe_layout_t;
 

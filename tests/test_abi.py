@@ -67,6 +67,18 @@ def test_layout_is_consistent(lib):
         moe.moe_workspace_layout(s, 4097)
 
 
+def test_dispatch_copy_region_only_for_small_topk(lib):
+    # k = 8: Linear1 gathers x through perm, so the blocked copy of x takes no bytes
+    L8 = moe.moe_workspace_layout(moe.make_shape(32, 7168, 2048, 8, 4096), 4096)
+    assert L8["xg"] == L8["xg_sf"] == L8["total"]
+    # k = 2: one H-byte row and its scale words per padded row
+    T, E, H = 4096, 8, 7168
+    L2 = moe.moe_workspace_layout(moe.make_shape(E, H, 2048, 2, T), T)
+    ppad = T * 2 + E * 255
+    assert L2["xg_sf"] - L2["xg"] >= ppad * H
+    assert L2["total"] - L2["xg_sf"] >= ppad * 4 * ((H + 511) // 512)
+
+
 def test_forward_host_errors(lib):
     s = moe.make_shape(4, 256, 512, 2, 64)
     ws_bytes = moe.moe_workspace_bytes(s)
