@@ -5,3 +5,4 @@ baseline may import or call anything in this package; the product path (the HIP
 library and its binding) never does, and this package never imports the product.
 """
 from .moe_oracle import *  # noqa: F401,F403
+from .gemm_oracle import *  # noqa: F401,F403
