@@ -1,4 +1,5 @@
-"""ctypes binding of libmoe.so (the C ABI declared in include/moe.h).
+"""ctypes binding of libmoe.so (the C ABI declared in include/moe.h and
+include/fp8_fp4_gemm.h).
 
 Argument marshalling only: every function passes device pointers, sizes and a HIP
 stream to the library and raises MoEError on a non-zero status. Tensors are torch
@@ -23,7 +24,10 @@ MOE_ERR_HIP = -6
 
 EXPORTED = ("moe_packed_weights_bytes", "moe_prepare_weights", "moe_workspace_bytes",
             "moe_forward", "moe_forward_events", "moe_workspace_layout", "moe_read_diagnostics",
-            "moe_status_string", "moe_version")
+            "moe_status_string", "moe_version",
+            "moe_gemm_packed_b_bytes", "moe_gemm_prepare_b", "moe_gemm_workspace_bytes",
+            "moe_fp8_fp4_gemm", "moe_m_grouped_fp8_fp4_gemm_contiguous",
+            "moe_m_grouped_fp8_fp4_gemm_masked", "moe_cast_to_fp8")
 
 
 class MoEError(RuntimeError):
@@ -81,6 +85,20 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_status_string.restype = ctypes.c_char_p
     lib.moe_version.argtypes = []
     lib.moe_version.restype = ctypes.c_int
+    lib.moe_gemm_packed_b_bytes.argtypes = [I32, I32, I32]
+    lib.moe_gemm_packed_b_bytes.restype = S
+    lib.moe_gemm_prepare_b.argtypes = [I32, I32, I32, P, P, P, S, P]
+    lib.moe_gemm_prepare_b.restype = ctypes.c_int
+    lib.moe_gemm_workspace_bytes.argtypes = [I32, I32]
+    lib.moe_gemm_workspace_bytes.restype = S
+    lib.moe_fp8_fp4_gemm.argtypes = [P, P, P, I32, I32, I32, P, P, S, P]
+    lib.moe_fp8_fp4_gemm.restype = ctypes.c_int
+    lib.moe_m_grouped_fp8_fp4_gemm_contiguous.argtypes = [P, P, P, P, I32, I32, I32, I32, P, P, S, P]
+    lib.moe_m_grouped_fp8_fp4_gemm_contiguous.restype = ctypes.c_int
+    lib.moe_m_grouped_fp8_fp4_gemm_masked.argtypes = [P, P, P, P, I32, I32, I32, I32, I32, P, P, S, P]
+    lib.moe_m_grouped_fp8_fp4_gemm_masked.restype = ctypes.c_int
+    lib.moe_cast_to_fp8.argtypes = [P, I32, I32, P, P, P]
+    lib.moe_cast_to_fp8.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -194,3 +212,60 @@ def moe_read_diagnostics(shape: moe_shape_t, workspace, stream=None):
                                                ctypes.byref(inv), counts, _stream(stream)),
            "moe_read_diagnostics")
     return inv.value, list(counts)
+
+
+# ---------------------------------------------------------------------------
+# FP8 x FP4 GEMMs and the FP8 cast (include/fp8_fp4_gemm.h)
+# ---------------------------------------------------------------------------
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def moe_gemm_packed_b_bytes(groups: int, n: int, k: int) -> int:
+    return load_library().moe_gemm_packed_b_bytes(int(groups), int(n), int(k))
+
+
+def moe_gemm_prepare_b(groups: int, n: int, k: int, b, b_sf, packed, stream=None) -> None:
+    _check(load_library().moe_gemm_prepare_b(int(groups), int(n), int(k), _ptr(b), _ptr(b_sf),
+                                             _ptr(packed), _nbytes(packed), _stream(stream)),
+           "moe_gemm_prepare_b")
+
+
+def moe_gemm_workspace_bytes(max_rows: int, groups: int) -> int:
+    return load_library().moe_gemm_workspace_bytes(int(max_rows), int(groups))
+
+
+def moe_fp8_fp4_gemm(d, a, a_sf, m: int, n: int, k: int, packed_b, workspace, stream=None) -> None:
+    _check(load_library().moe_fp8_fp4_gemm(_ptr(d), _ptr(a), _ptr(a_sf), int(m), int(n), int(k),
+                                           _ptr(packed_b), _ptr(workspace), _nbytes(workspace),
+                                           _stream(stream)), "moe_fp8_fp4_gemm")
+
+
+def moe_m_grouped_fp8_fp4_gemm_contiguous(d, a, a_sf, group_of_row, m: int, groups: int, n: int,
+                                          k: int, packed_b, workspace, stream=None) -> None:
+    _check(load_library().moe_m_grouped_fp8_fp4_gemm_contiguous(
+        _ptr(d), _ptr(a), _ptr(a_sf), _ptr(group_of_row), int(m), int(groups), int(n), int(k),
+        _ptr(packed_b), _ptr(workspace), _nbytes(workspace), _stream(stream)),
+        "moe_m_grouped_fp8_fp4_gemm_contiguous")
+
+
+def moe_m_grouped_fp8_fp4_gemm_masked(d, a, a_sf, masked_m, groups: int, max_m: int,
+                                      expected_m: int, n: int, k: int, packed_b, workspace,
+                                      stream=None) -> None:
+    _check(load_library().moe_m_grouped_fp8_fp4_gemm_masked(
+        _ptr(d), _ptr(a), _ptr(a_sf), _ptr(masked_m), int(groups), int(max_m), int(expected_m),
+        int(n), int(k), _ptr(packed_b), _ptr(workspace), _nbytes(workspace), _stream(stream)),
+        "moe_m_grouped_fp8_fp4_gemm_masked")
+
+
+def moe_cast_to_fp8(x, rows: int, cols: int, x_fp8, x_sf, stream=None) -> None:
+    _check(load_library().moe_cast_to_fp8(_ptr(x), int(rows), int(cols), _ptr(x_fp8), _ptr(x_sf),
+                                          _stream(stream)), "moe_cast_to_fp8")
+
+
+def gemm_call_raw(name: str, *args) -> int:
+    """Unchecked call of one of the GEMM / cast entry points with raw arguments; returns the
+    status (for error-path tests)."""
+    return getattr(load_library(), name)(*args)

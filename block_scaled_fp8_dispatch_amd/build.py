@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
-SOURCES = ["moe_api.hip", "route.hip", "pack.hip", "gemm.hip", "combine.hip"]
+SOURCES = ["moe_api.hip", "gemm_api.hip", "route.hip", "pack.hip", "gemm.hip", "combine.hip", "cast.hip"]
 ARCH = "gfx950"
 
 

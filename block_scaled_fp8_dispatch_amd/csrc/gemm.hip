@@ -9,6 +9,9 @@
 //   Linear2 (step 4): rows of h8 x packed W2; the epilogue multiplies each row by its
 //     top-k weight and writes it, as bf16, to the staging row of its (token, slot) (the
 //     combine of step 5 then sums a token's slots in slot order, without atomics).
+//   Plain GEMM (section 4.3's FP8 x FP4 GEMM, and its M-grouped contiguous and masked
+//     forms): rows of A named by the row list x packed B of the tile's group; the epilogue
+//     writes each row, as bf16, to the same row of D, skipping columns past N.
 //
 // Tiling. A workgroup of 4 waves owns a BM x 256 output tile of one expert's rows (row
 // tiles come from the dispatch tile list; an expert's group is padded to BM rows).
@@ -149,7 +152,7 @@ struct Cfg {
     static_assert(FM >= 2 && FM % 2 == 0, "mid-step split");
     static_assert(MODE != 1 || WAVES_N * (FN / 2) == 8, "gate/up pairing");
     static_assert(MODE != 1 || 4 * WAVES_N * BM <= STAGE_BYTES, "epilogue fits a slot");
-    static_assert(MODE != 2 || FN == 8 || FN == 4, "one 16- or 8-byte store per row");
+    static_assert(MODE == 1 || FN == 8 || FN == 4, "one 16- or 8-byte store per row");
 };
 
 template <int BM, int WAVES_M, int WAVES_N, int MODE>
@@ -220,13 +223,14 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
     // ks sits at (tile block + ks) * hblk * 128 + (row in block) * 128, the per-step part in
     // the uniform offset, and its scale row is the padded row. Otherwise (Linear1 without a
     // dispatch copy) A is x itself, row-major, its rows the tokens perm names (padding rows
-    // read token 0 and are never stored).
-    const bool blocked = MODE == 2 || args.a_blocked != 0;
+    // read token 0 and are never stored); in the plain GEMM perm names A rows directly.
+    const bool blocked = MODE == 2 || (MODE == 1 && args.a_blocked != 0);
     const int NKB = args.K / kBK;
     const uint32_t a_kstep = blocked ? (uint32_t)args.hblk * kBK : (uint32_t)kBK;
     auto src_row = [&](int r) __attribute__((always_inline)) -> uint32_t {
         const int slot = args.perm[row0 + r];
-        return slot >= 0 ? (uint32_t)(slot / args.topk) : 0u;
+        if (slot < 0) return 0u;
+        return MODE == 3 ? (uint32_t)slot : (uint32_t)(slot / args.topk);
     };
     uint32_t a_off[A_DMA];
 #pragma unroll
@@ -463,9 +467,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
         } else {
             // Lane column l of the wave's fragments wn*FN .. wn*FN+FN-1 holds output columns
             // col0 .. col0+FN-1 (the packed W2 interleaves its rows so). Each row is scaled by
-            // its slot's top-k weight, rounded to bf16 (round to nearest even) and stored as
-            // one FN*2-byte chunk per lane into the stage row of its slot; padding rows are
-            // skipped. All slot and weight loads are issued before any is needed.
+            // its slot's top-k weight (Linear2; 1 in the plain GEMM), rounded to bf16 (round
+            // to nearest even) and stored as one FN*2-byte chunk per lane into the stage row
+            // of its slot (the plain GEMM: row of D); padding rows are skipped, and in the
+            // plain GEMM so are columns past N (N is a multiple of 16, so a lane's chunk is
+            // wholly in or out). All slot and weight loads are issued before any is needed.
             typedef float v2f __attribute__((ext_vector_type(2)));
             typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
             const int l = lane & 15;
@@ -481,7 +487,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
             for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    wt[fm][r] = args.topk_weights[slot[fm][r] >= 0 ? slot[fm][r] : 0];
+                    wt[fm][r] = MODE == 2 ? args.topk_weights[slot[fm][r] >= 0 ? slot[fm][r] : 0] : 1.0f;
+            const bool col_ok = MODE != 3 || nt * kBN + col0 < args.out_cols;
             uint16_t* sbase = args.stage + nt * kBN + col0;
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm) {
@@ -493,7 +500,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
                         const v2f x = {acc[fm][2 * p][r] * wt[fm][r], acc[fm][2 * p + 1][r] * wt[fm][r]};
                         pk[p] = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, v2bf));
                     }
-                    if (slot[fm][r] >= 0) {
+                    if (slot[fm][r] >= 0 && col_ok) {
                         uint16_t* dst = sbase + (size_t)slot[fm][r] * args.out_cols;
                         if constexpr (FN == 8)
                             *reinterpret_cast<v4i*>(dst) = (v4i){(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3]};
@@ -574,6 +581,9 @@ hipError_t launch_linear1(int block_m, const GemmArgs& a, hipStream_t stream) {
 }
 hipError_t launch_linear2(int block_m, const GemmArgs& a, hipStream_t stream) {
     return launch_mode<2>(block_m, a, stream);
+}
+hipError_t launch_gemm_plain(int block_m, const GemmArgs& a, hipStream_t stream) {
+    return launch_mode<3>(block_m, a, stream);
 }
 
 }  // namespace moe

@@ -61,7 +61,7 @@ struct GemmArgs {
     int a_sf_stride;           // bytes per A scale row
     int K;                     // reduction length (multiple of 128)
     int topk;                  // a_blocked == 0: slot -> token = slot / topk
-    const int32_t* perm;
+    const int32_t* perm;       // per padded row: slot (MoE) or A/D row (plain GEMM); -1 padding
     const int32_t* meta;       // meta[0] = number of M tiles in use
     const int32_t* tile_expert;
     const int32_t* tile_row0;
@@ -85,7 +85,7 @@ struct GemmArgs {
     uint8_t* h_sf;
     int h_stride;              // = I
     int h_sf_stride;
-    // Linear2 outputs
+    // Linear2 outputs (plain GEMM: stage = D, out_cols = N, the row stride of D)
     uint16_t* stage;
     const float* topk_weights;
     int out_cols;              // = H
@@ -93,6 +93,32 @@ struct GemmArgs {
 
 hipError_t launch_linear1(int block_m, const GemmArgs& a, hipStream_t stream);
 hipError_t launch_linear2(int block_m, const GemmArgs& a, hipStream_t stream);
+// Plain FP8 x FP4 GEMM over a row list: D[perm[p]] = bf16(A[perm[p]] . B_g^T)
+hipError_t launch_gemm_plain(int block_m, const GemmArgs& a, hipStream_t stream);
+
+// Packed B of the plain GEMMs ([G][N][K] FP4, the W2 layout): N padded to 256-row tiles
+// with zero rows
+struct PackedBLayout {
+    size_t data, scales, total;          // byte offsets
+    size_t d_group, d_ntile;             // bytes
+    size_t s_group, s_ntile;             // bytes
+    int n_tiles;
+};
+PackedBLayout packed_b_layout(int G, int N, int K);
+hipError_t launch_pack_b(int G, int N, int K, const PackedBLayout& L, const uint8_t* b,
+                         const uint8_t* b_sf, uint8_t* packed, hipStream_t stream);
+
+// Row list and tile list of the plain GEMMs without a routing pass (route.hip):
+// kind 0 = dense (G = 1, M rows), kind 1 = masked (group g's rows g*max_m + i,
+// i < clamp(masked_m[g], 0, max_m)). Each group is padded to BM rows.
+hipError_t launch_gemm_layout(int kind, int M, int G, int max_m, const int32_t* masked_m,
+                              int block_m, int pad_rows_cap, int32_t* perm,
+                              int32_t* tile_expert, int32_t* tile_row0, int32_t* meta,
+                              hipStream_t stream);
+
+// FP8 cast of bf16 rows (cast.hip)
+hipError_t launch_cast_fp8(const uint16_t* x, int rows, int cols, uint8_t* q, uint8_t* sf,
+                           hipStream_t stream);
 
 // Dispatch copy (route.hip): the x row and scales of each padded row's token into the
 // blocked A layout of Linear1 (zero on padding rows)

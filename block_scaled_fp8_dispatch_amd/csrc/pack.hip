@@ -25,6 +25,10 @@
 //   W2 scales [E][H/256][ceil(I/512)][16][64] u32
 // Every byte of the input lands in exactly one place; scale bytes of K steps past the
 // end of K are zero.
+//
+// The plain GEMMs' B ([G][N][K], section 4.3 of the same page) takes the W2 layout with N
+// in place of H; when N is not a multiple of 256 the last column tile is completed with
+// zero rows (data and scale bytes 0).
 #include "moe_internal.h"
 
 namespace moe {
@@ -45,6 +49,7 @@ __device__ inline int l2_row(int f, int lane, int nt) {
 __global__ __launch_bounds__(256) void pack_data_kernel(
     const uint8_t* __restrict__ src, uint8_t* __restrict__ dst, size_t n_chunks,
     int rows_per_expert, int src_row_bytes, int nks, int n_tiles, int l1_gate_up, int I) {
+    // rows at or past rows_per_expert (the zero padding of a last partial tile) are zeros
     const size_t idx = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
     if (idx >= n_chunks) return;
     const int lane = (int)(idx & 63);
@@ -55,6 +60,10 @@ __global__ __launch_bounds__(256) void pack_data_kernel(
     const int nt = (int)(rest % n_tiles);
     const int e = (int)(rest / n_tiles);
     const int row = l1_gate_up ? l1_row(f, lane, nt, I) : l2_row(f, lane, nt);
+    if (row >= rows_per_expert) {
+        *reinterpret_cast<uint4*>(dst + idx * 16) = make_uint4(0, 0, 0, 0);
+        return;
+    }
     const uint8_t* s = src + ((size_t)e * rows_per_expert + row) * src_row_bytes + ks * 64 +
                        (lane >> 4) * 16;
     *reinterpret_cast<uint4*>(dst + idx * 16) = *reinterpret_cast<const uint4*>(s);
@@ -74,6 +83,10 @@ __global__ __launch_bounds__(256) void pack_scale_kernel(
     const int nt = (int)(rest % n_tiles);
     const int e = (int)(rest / n_tiles);
     const int row = l1_gate_up ? l1_row(f, lane, nt, I) : l2_row(f, lane, nt);
+    if (row >= rows_per_expert) {
+        dst[idx] = 0;
+        return;
+    }
     const uint8_t* s = src_sf + ((size_t)e * rows_per_expert + row) * sf_row_bytes;
     uint32_t w = 0;
     for (int b = 0; b < 4; ++b) {
@@ -132,6 +145,34 @@ hipError_t launch_pack(const moe_shape_t& s, const PackedLayout& L, const uint8_
             w2_sf, reinterpret_cast<uint32_t*>(packed + L.w2s), m, H, I / 32, nks2, nkb2, nt2, 0,
             I);
     }
+    return hipGetLastError();
+}
+
+PackedBLayout packed_b_layout(int G, int N, int K) {
+    PackedBLayout L{};
+    L.n_tiles = cdiv(N, 256);
+    const size_t nks = K / 128, nkb = cdiv(K, 512);
+    L.d_ntile = nks * kBTileBytes;
+    L.d_group = L.n_tiles * L.d_ntile;
+    L.s_ntile = nkb * kBScaleBlockBytes;
+    L.s_group = L.n_tiles * L.s_ntile;
+    size_t off = 0;
+    L.data = off; off = align_up(off + (size_t)G * L.d_group, 256);
+    L.scales = off; off = align_up(off + (size_t)G * L.s_group, 256);
+    L.total = off;
+    return L;
+}
+
+hipError_t launch_pack_b(int G, int N, int K, const PackedBLayout& L, const uint8_t* b,
+                         const uint8_t* b_sf, uint8_t* packed, hipStream_t stream) {
+    const int nks = K / 128, nkb = cdiv(K, 512), nt = L.n_tiles;
+    const int T = 256;
+    const size_t n = (size_t)G * nt * nks * 1024;
+    pack_data_kernel<<<(unsigned)((n + T - 1) / T), T, 0, stream>>>(b, packed + L.data, n, N, K / 2,
+                                                                     nks, nt, 0, 0);
+    const size_t m = (size_t)G * nt * nkb * 1024;
+    pack_scale_kernel<<<(unsigned)((m + T - 1) / T), T, 0, stream>>>(
+        b_sf, reinterpret_cast<uint32_t*>(packed + L.scales), m, N, K / 32, nks, nkb, nt, 0, 0);
     return hipGetLastError();
 }
 

@@ -320,7 +320,82 @@ __global__ __launch_bounds__(256) void gather_kernel(const uint8_t* __restrict__
     }
 }
 
+// Row and tile lists of the dense and masked plain GEMMs (no routing pass: the groups'
+// rows are known by position). Every workgroup scans the groups' padded sizes (group g:
+// c_g rows, ceil(c_g / BM) tiles; dense: one group of M rows; masked: c_g =
+// clamp(masked_m[g], 0, max_m)), then writes perm for its share of padded rows: A row
+// (g * max_m + i for masked, i for dense) or -1 on padding. Workgroup 0 also writes the
+// tile list and meta[0].
+constexpr int kLayoutRows = 16384;
+
+__device__ inline int upper_group(const int* off, int G, int v) {
+    // largest g in [0, G) with off[g] <= v
+    int lo = 0, hi = G - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (off[mid] <= v) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+__global__ __launch_bounds__(1024) void gemm_layout_kernel(int kind, int M, int G, int max_m,
+                                                          const int32_t* __restrict__ masked_m,
+                                                          int block_m, int32_t* __restrict__ perm,
+                                                          int32_t* __restrict__ tile_expert,
+                                                          int32_t* __restrict__ tile_row0,
+                                                          int32_t* __restrict__ meta) {
+    __shared__ int warp_sums[16];
+    __shared__ int toff[MOE_MAX_EXPERTS + 1];     // first tile of each group
+    __shared__ int cnt[MOE_MAX_EXPERTS];
+    const int tid = threadIdx.x;
+    int c = 0;
+    if (tid < G) {
+        if (kind == 0) {
+            c = M;
+        } else {
+            c = masked_m[tid];
+            c = c < 0 ? 0 : (c > max_m ? max_m : c);
+        }
+    }
+    const int nt = (c + block_m - 1) / block_m;
+    int total = 0;
+    const int excl = block_exclusive_scan_1024(nt, warp_sums, &total);
+    if (tid < G) {
+        toff[tid] = excl;
+        cnt[tid] = c;
+    }
+    if (tid == 0) toff[G] = total;
+    __syncthreads();
+    const int rows = total * block_m;
+    const int r0 = blockIdx.x * kLayoutRows;
+    for (int p = r0 + tid; p < rows && p < r0 + kLayoutRows; p += 1024) {
+        const int t = p / block_m;
+        const int g = upper_group(toff, G, t);
+        const int i = p - toff[g] * block_m;
+        perm[p] = i < cnt[g] ? (kind == 0 ? i : g * max_m + i) : -1;
+    }
+    if (blockIdx.x == 0) {
+        for (int t = tid; t < total; t += 1024) {
+            const int g = upper_group(toff, G, t);
+            tile_expert[t] = g;
+            tile_row0[t] = t * block_m;
+        }
+        if (tid == 0) meta[0] = total;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_gemm_layout(int kind, int M, int G, int max_m, const int32_t* masked_m,
+                              int block_m, int pad_rows_cap, int32_t* perm,
+                              int32_t* tile_expert, int32_t* tile_row0, int32_t* meta,
+                              hipStream_t stream) {
+    if (G < 1 || G > MOE_MAX_EXPERTS) return hipErrorInvalidValue;
+    const int grid = pad_rows_cap > 0 ? cdiv(pad_rows_cap, kLayoutRows) : 1;
+    gemm_layout_kernel<<<grid, 1024, 0, stream>>>(kind, M, G, max_m, masked_m, block_m, perm,
+                                                  tile_expert, tile_row0, meta);
+    return hipGetLastError();
+}
 
 hipError_t launch_gather(const uint8_t* x, const uint8_t* x_sf, const int32_t* perm,
                          const int32_t* meta, int k, int H, int sfs, int hblk, int max_rows,

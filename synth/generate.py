@@ -208,3 +208,102 @@ def make_inputs(cfg: MoEConfig, seed: int = 0, device="cpu") -> MoEInputs:
 
 def custom_config(name="custom", **kw) -> MoEConfig:
     return MoEConfig(name, **kw)
+
+
+# ---------------------------------------------------------------------------
+# Inputs of the standalone FP8 x FP4 GEMMs and of the FP8 cast
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass(frozen=True)
+class GemmConfig:
+    """One GEMM workload. layout: "dense" (M rows, one group), "contiguous" (M rows in G
+    groups, each group's segment padded to a multiple of 128 rows with rows of group -1),
+    "masked" (G groups of up to M = max_m rows, expected_m rows per group on average)."""
+    name: str
+    layout: str
+    M: int
+    N: int
+    K: int
+    G: int = 1
+    expected_m: int = 0
+
+    @property
+    def rows(self) -> int:
+        return self.G * self.M if self.layout == "masked" else self.M
+
+
+# Shapes of the GEMM table on juejin.cn/post/7631516744872673307 (section "性能实测"): a
+# decode-sized dense GEMM (M=64, N=2112, K=7168), a 4-group contiguous MoE GEMM (M=8192,
+# N=4096; K not printed, taken as 7168) and a large dense GEMM (M=4096, K=16384; N not
+# printed, taken as 4096). The masked case has no printed shape: it is the decode-sized
+# share of c1 (32 groups of about 32 rows, N = 2*2048, K = 7168).
+GEMM_CONFIGS = {
+    "g_tiny": GemmConfig("g_tiny", "dense", M=77, N=272, K=384),
+    "g_dense_decode": GemmConfig("g_dense_decode", "dense", M=64, N=2112, K=7168),
+    "g_contig4": GemmConfig("g_contig4", "contiguous", M=8192, N=4096, K=7168, G=4),
+    "g_dense_large": GemmConfig("g_dense_large", "dense", M=4096, N=4096, K=16384),
+    "g_masked_decode": GemmConfig("g_masked_decode", "masked", M=64, N=4096, K=7168, G=32,
+                                  expected_m=32),
+}
+
+_TID_GA, _TID_GB, _TID_GLAYOUT, _TID_BF16 = 300, 400, 500, 600
+
+
+@dataclasses.dataclass
+class GemmInputs:
+    cfg: GemmConfig
+    a: torch.Tensor            # u8 [rows, K] e4m3 (masked: [G, max_m, K])
+    a_sf: torch.Tensor         # u8 [rows, 4*ceil(K/512)]
+    b: torch.Tensor            # u8 [G, N, K/2] E2M1 pairs
+    b_sf: torch.Tensor         # u8 [G, N, K/32]
+    group_of_row: Optional[torch.Tensor] = None   # i32 [M] (contiguous)
+    masked_m: Optional[torch.Tensor] = None       # i32 [G] (masked)
+
+
+def make_gemm_inputs(cfg: GemmConfig, seed: int = 0, device="cpu", sigma: float = 0.02) -> GemmInputs:
+    """A ~ N(0,1) cast to e4m3 per 1x128; B ~ N(0, sigma) cast to E2M1 per 1x32 (as the MoE
+    activations and weights). Contiguous: group g owns segment g of M/G rows (the last one
+    takes the remainder), whose last 0..127 rows are padding (-1). Masked: counts uniform in
+    [expected_m/2, 3*expected_m/2], clamped to max_m."""
+    rows, K, N, G = cfg.rows, cfg.K, cfg.N, cfg.G
+    ga = _gen(device, seed, _TID_GA)
+    a_parts, sf_parts = [], []
+    for r0 in range(0, rows, 8192):
+        r1 = min(rows, r0 + 8192)
+        q, s = cast_fp8_blocks(torch.randn(r1 - r0, K, generator=ga, device=device))
+        a_parts.append(q)
+        sf_parts.append(s)
+    a = torch.cat(a_parts) if a_parts else torch.empty(0, K, dtype=torch.uint8, device=device)
+    a_sf = torch.cat(sf_parts) if sf_parts else torch.empty(0, 4 * ((K + 511) // 512), dtype=torch.uint8, device=device)
+    b = torch.empty(G, N, K // 2, dtype=torch.uint8, device=device)
+    b_sf = torch.empty(G, N, K // 32, dtype=torch.uint8, device=device)
+    for g in range(G):
+        gb = _gen(device, seed, _TID_GB + g)
+        for r0 in range(0, N, 8192):
+            r1 = min(N, r0 + 8192)
+            b[g, r0:r1], b_sf[g, r0:r1] = cast_fp4_blocks(torch.randn(r1 - r0, K, generator=gb, device=device) * sigma)
+    out = GemmInputs(cfg, a, a_sf, b, b_sf)
+    gl = _gen("cpu", seed, _TID_GLAYOUT)
+    if cfg.layout == "contiguous":
+        grp = torch.full((cfg.M,), -1, dtype=torch.int32)
+        seg = cfg.M // G
+        for g in range(G):
+            s0 = g * seg
+            s1 = cfg.M if g == G - 1 else s0 + seg
+            pad = int(torch.randint(0, 128, (1,), generator=gl))
+            grp[s0:max(s0, s1 - pad)] = g
+        out.group_of_row = grp.to(device)
+    elif cfg.layout == "masked":
+        e = max(cfg.expected_m, 1)
+        cnt = torch.randint(e // 2, e + e // 2 + 1, (G,), generator=gl).clamp(max=cfg.M)
+        out.masked_m = cnt.to(torch.int32).to(device)
+        out.a = out.a.view(G, cfg.M, K)
+        out.a_sf = out.a_sf.view(G, cfg.M, -1)
+    return out
+
+
+def make_bf16_activations(rows: int, cols: int, seed: int = 0, device="cpu") -> torch.Tensor:
+    """bf16 [rows, cols] ~ N(0, 1) (the activation of the explainer's usage example, section
+    9.2, before it is cast to FP8)."""
+    g = _gen(device, seed, _TID_BF16)
+    return torch.randn(rows, cols, generator=g, device=device).to(torch.bfloat16)

@@ -1,4 +1,4 @@
-"""The C-ABI library: it loads, exports every symbol include/moe.h declares, and rejects bad
+"""The C-ABI library: it loads, exports every symbol include/*.h declares, and rejects bad
 arguments on the host before launching anything (no GPU needed: no call below reaches
 the device)."""
 import ctypes
@@ -13,9 +13,13 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def _header_functions():
-    text = open(os.path.join(ROOT, "include", "moe.h")).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    names = set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text))
+    names = set()
+    inc = os.path.join(ROOT, "include")
+    for h in sorted(os.listdir(inc)):
+        if not h.endswith(".h"):
+            continue
+        text = re.sub(r"/\*.*?\*/", "", open(os.path.join(inc, h)).read(), flags=re.S)
+        names |= set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text))
     return names
 
 
@@ -122,3 +126,61 @@ def test_missing_library_fails_loudly(tmp_path):
             _lib.load_library(str(tmp_path / "nope.so"))
     finally:
         _lib._lib = saved
+
+
+def test_gemm_sizes_and_host_errors(lib):
+    G, N, K = 4, 2112, 7168
+    nb = moe.moe_gemm_packed_b_bytes(G, N, K)
+    # N padded to 9 tiles of 256 rows: FP4 data + one 32-bit scale word per lane, fragment and 512 K
+    assert nb == G * 9 * 256 * K // 2 + G * 9 * ((K + 511) // 512) * 16 * 64 * 4
+    for bad in ((0, 256, 256), (1025, 256, 256), (1, 8, 256), (1, 264, 256), (1, 256, 128),
+                (1, 256, 320)):
+        assert moe.moe_gemm_packed_b_bytes(*bad) == 0
+    assert moe.moe_gemm_workspace_bytes(-1, 1) == 0 and moe.moe_gemm_workspace_bytes(10, 0) == 0
+    wsb = moe.moe_gemm_workspace_bytes(64, 1)
+    A = 0x10000
+    call = moe.gemm_call_raw
+    P = lambda **o: dict(dict(d=A, a=A, asf=A, b=A, ws=A), **o)
+
+    def dense(m=64, n=256, k=512, wb=wsb, **o):
+        p = P(**o)
+        return call("moe_fp8_fp4_gemm", p["d"], p["a"], p["asf"], m, n, k, p["b"], p["ws"], wb, None)
+
+    assert dense(d=None) == moe.MOE_ERR_NULL
+    assert dense(n=100) == moe.MOE_ERR_SHAPE
+    assert dense(k=384 + 64) == moe.MOE_ERR_SHAPE
+    assert dense(a=A + 4) == moe.MOE_ERR_ALIGN
+    assert dense(m=-1) == moe.MOE_ERR_TOKENS
+    assert dense(m=2 ** 24, k=512) == moe.MOE_ERR_TOKENS        # m * k >= 2^32
+    assert dense(wb=wsb - 1) == moe.MOE_ERR_WORKSPACE
+    assert dense(m=0) == moe.MOE_OK
+
+    def contig(m=64, groups=3, wb=None, **o):
+        p = P(**o)
+        wb = moe.moe_gemm_workspace_bytes(m, groups) if wb is None else wb
+        return call("moe_m_grouped_fp8_fp4_gemm_contiguous", p["d"], p["a"], p["asf"], A, m, groups,
+                    256, 512, p["b"], p["ws"], wb, None)
+
+    assert contig(groups=0, wb=1 << 20) == moe.MOE_ERR_SHAPE
+    assert contig(ws=None) == moe.MOE_ERR_NULL
+    assert contig(wb=moe.moe_gemm_workspace_bytes(64, 3) - 1) == moe.MOE_ERR_WORKSPACE
+    assert contig(m=0) == moe.MOE_OK
+
+    def masked(groups=3, max_m=16, wb=None, **o):
+        p = P(**o)
+        wb = moe.moe_gemm_workspace_bytes(max(groups * max_m, 0), max(groups, 1)) if wb is None else wb
+        return call("moe_m_grouped_fp8_fp4_gemm_masked", p["d"], p["a"], p["asf"], A, groups, max_m, 8,
+                    256, 512, p["b"], p["ws"], wb, None)
+
+    assert masked(max_m=-1, wb=1 << 20) == moe.MOE_ERR_TOKENS
+    assert masked(wb=moe.moe_gemm_workspace_bytes(48, 3) - 1) == moe.MOE_ERR_WORKSPACE
+    assert masked(d=A + 2) == moe.MOE_ERR_ALIGN
+    assert masked(max_m=0) == moe.MOE_OK
+
+    assert call("moe_cast_to_fp8", A, 4, 200, A, A, None) == moe.MOE_ERR_SHAPE
+    assert call("moe_cast_to_fp8", A, -1, 256, A, A, None) == moe.MOE_ERR_TOKENS
+    assert call("moe_cast_to_fp8", None, 4, 256, A, A, None) == moe.MOE_ERR_NULL
+    assert call("moe_cast_to_fp8", A, 4, 256, A + 8, A, None) == moe.MOE_ERR_ALIGN
+    assert call("moe_cast_to_fp8", A, 0, 256, A, A, None) == moe.MOE_OK
+    assert call("moe_gemm_prepare_b", 1, 256, 512, A, A, A, moe.moe_gemm_packed_b_bytes(1, 256, 512) - 1,
+                None) == moe.MOE_ERR_WORKSPACE
