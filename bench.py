@@ -9,6 +9,11 @@ explainer's worked shape, chenxutan.com/d/1930 section 3.3).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c2]
 
+Other workloads (not the default line): --config g_dense_decode | g_contig4 | g_dense_large |
+g_masked_decode times one call of the standalone FP8 x FP4 GEMM of that shape (section 4.3's
+GEMM; the shapes of juejin.cn/post/7631516744872673307 "性能实测"), and --config cast times
+the FP8 cast of 8192 x 7168 bf16 rows.
+
 Prints one JSON line. FLOP = 6*T*k*H*I over valid slots only (2*P*H*2I for Linear1 plus
 2*P*I*H for Linear2). Stage times come from HIP events the library records on the
 launch stream between its kernels; the roofline object is for Linear1, the dominant
@@ -89,6 +94,136 @@ def cpu_baseline(inp_cpu: dict, cfg, n_tokens: int):
             "seconds": dt}
 
 
+def _timed(call, steps, warmup):
+    """Mean ms of `call` over `steps` calls between two events on the launch stream, after
+    `warmup` untimed calls; synchronised on both sides."""
+    import torch
+    for _ in range(warmup):
+        call()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(steps):
+        call()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps, time.perf_counter() - t0
+
+
+def _threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    except Exception:
+        return os.cpu_count() or 1
+
+
+def bench_gemm(args, gcfg):
+    """One standalone GEMM call per step (its layout or routing kernel plus the GEMM)."""
+    import numpy as np
+    import torch
+
+    import block_scaled_fp8_dispatch_amd as moe
+    import oracle
+    from synth import make_gemm_inputs
+    c = gcfg
+    inp = make_gemm_inputs(c, seed=args.seed, device="cuda")
+    packed = torch.empty(moe.moe_gemm_packed_b_bytes(c.G, c.N, c.K), dtype=torch.uint8, device="cuda")
+    moe.moe_gemm_prepare_b(c.G, c.N, c.K, inp.b, inp.b_sf, packed)
+    ws = torch.empty(moe.moe_gemm_workspace_bytes(c.rows, c.G), dtype=torch.uint8, device="cuda")
+    d = torch.empty(c.rows, c.N, dtype=torch.int16, device="cuda")
+
+    def call():
+        if c.layout == "dense":
+            moe.moe_fp8_fp4_gemm(d, inp.a, inp.a_sf, c.M, c.N, c.K, packed, ws)
+        elif c.layout == "contiguous":
+            moe.moe_m_grouped_fp8_fp4_gemm_contiguous(d, inp.a, inp.a_sf, inp.group_of_row, c.M, c.G,
+                                                      c.N, c.K, packed, ws)
+        else:
+            moe.moe_m_grouped_fp8_fp4_gemm_masked(d, inp.a, inp.a_sf, inp.masked_m, c.G, c.M,
+                                                  c.expected_m, c.N, c.K, packed, ws)
+
+    ms, wall = _timed(call, args.steps, args.warmup)
+    if c.layout == "dense":
+        rows = c.M
+    elif c.layout == "contiguous":
+        rows = int((inp.group_of_row >= 0).sum())
+    else:
+        rows = int(inp.masked_m.clamp(0, c.M).sum())
+    flop = 2.0 * rows * c.N * c.K
+    tflops = flop / (ms * 1e-3) / 1e12
+    # algorithmic bytes: B and its scales once, the computed A rows and scales, D rows
+    alg = c.G * c.N * (c.K // 2 + c.K // 32) + rows * (c.K + 4 * ((c.K + 511) // 512)) + 2 * rows * c.N
+    gbs = alg / (ms * 1e-3) / 1e9
+    hbm_bound = flop / alg < PEAK_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    roof = ({"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+             "frac": round(gbs / PEAK_HBM_GBS, 4)} if hbm_bound else
+            {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
+             "frac": round(tflops / PEAK_TFLOPS, 4)})
+    roof.update({"kernel": "one GEMM call (layout or routing kernel + grouped GEMM in plain mode)",
+                 "traffic": None})
+    out = {"metric": "FP8×FP4 GEMM TFLOPS & % of MI355X FP8 MFMA peak (1 GPU)", "value": round(tflops, 2),
+           "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "fp8e4m3 x fp4e2m1 -> f32 accumulate, bf16 out",
+           "data": "synthetic (seeded; A~N(0,1) FP8 1x128 UE8M0, B~N(0,0.02) FP4 1x32 UE8M0)",
+           "config": {"workload": f"{c.name}: {c.layout} GEMM M={c.M} N={c.N} K={c.K} groups={c.G}"
+                                  + (f" expected_m={c.expected_m}" if c.layout == "masked" else ""),
+                      "layout": c.layout, "M": c.M, "N": c.N, "K": c.K, "groups": c.G, "rows_computed": rows},
+           "alg_hbm_gbs": round(gbs, 1), "wall_s_timed": round(wall, 3), "roofline": roof, "cpu_baseline": None}
+    if not args.no_cpu_baseline:
+        # the oracle on the first rows of group 0 (about 10-30 s of CPU work is the aim)
+        n = max(1, min(rows, int(6e10 / (2.0 * c.N * c.K))))
+        a = inp.a.reshape(-1, c.K)[:n].cpu().numpy()
+        a_sf = inp.a_sf.reshape(-1, inp.a_sf.shape[-1])[:n].cpu().numpy()
+        b, b_sf = inp.b[0].cpu().numpy(), inp.b_sf[0].cpu().numpy()
+        t0 = time.perf_counter()
+        oracle.fp8_fp4_gemm(a, a_sf, b, b_sf, c.K)
+        dt = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": 2.0 * n * c.N * c.K / dt / 1e12, "unit": "TFLOP/s",
+                               "cores": int(_threads()), "kind": "oracle",
+                               "sample": f"first {n} rows against group 0's B, {dt:.1f} s; numpy fp64"}
+    print(json.dumps(out), flush=True)
+
+
+def bench_cast(args, rows=8192, cols=7168):
+    import torch
+
+    import block_scaled_fp8_dispatch_amd as moe
+    import oracle
+    from synth import make_bf16_activations
+    x = make_bf16_activations(rows, cols, seed=args.seed, device="cuda")
+    q = torch.empty(rows, cols, dtype=torch.uint8, device="cuda")
+    sf = torch.empty(rows, 4 * ((cols + 511) // 512), dtype=torch.uint8, device="cuda")
+    ms, wall = _timed(lambda: moe.moe_cast_to_fp8(x, rows, cols, q, sf), args.steps, args.warmup)
+    alg = rows * cols * 3 + rows * sf.shape[1]
+    gbs = alg / (ms * 1e-3) / 1e9
+    out = {"metric": "FP8 cast GB/s (bf16 -> e4m3 + UE8M0 per 1x128, 1 GPU)", "value": round(gbs, 1),
+           "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16 -> fp8e4m3", "data": "synthetic (seeded; x~N(0,1) bf16)",
+           "config": {"workload": f"cast: {rows} x {cols} bf16", "rows": rows, "cols": cols},
+           "wall_s_timed": round(wall, 3),
+           "roofline": {"bound": "hbm", "kernel": "cast_fp8_kernel", "achieved": round(gbs, 1),
+                        "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                        "traffic": None},
+           "cpu_baseline": None}
+    if not args.no_cpu_baseline:
+        n = 1024
+        bits = x[:n].view(torch.int16).cpu().numpy().view("uint16")
+        t0 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t0 < 10.0:
+            oracle.cast_to_fp8(bits)
+            reps += 1
+        dt = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": reps * n * (cols * 3 + sf.shape[1]) / dt / 1e9, "unit": "GB/s",
+                               "cores": int(_threads()), "kind": "oracle",
+                               "sample": f"{reps} casts of the first {n} rows, {dt:.1f} s; numpy fp64"}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -99,10 +234,14 @@ def main():
     import torch
 
     import block_scaled_fp8_dispatch_amd as moe
-    from synth import CONFIGS, make_inputs
+    from synth import CONFIGS, GEMM_CONFIGS, make_inputs
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     moe.load_library()
+    if args.config in GEMM_CONFIGS:
+        return bench_gemm(args, GEMM_CONFIGS[args.config])
+    if args.config == "cast":
+        return bench_cast(args)
     cfg = CONFIGS[args.config]
     dev = "cuda"
     if args.copy_calibration_mib:
