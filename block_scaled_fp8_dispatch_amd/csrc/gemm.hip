@@ -11,7 +11,10 @@
 //     combine of step 5 then sums a token's slots in slot order, without atomics).
 //   Plain GEMM (section 4.3's FP8 x FP4 GEMM, and its M-grouped contiguous and masked
 //     forms): rows of A named by the row list x packed B of the tile's group; the epilogue
-//     writes each row, as bf16, to the same row of D, skipping columns past N.
+//     writes each row, as bf16, to the same row of D, skipping columns past N. With few
+//     output tiles (a decode-sized dense GEMM) the K steps are split over several
+//     workgroups: each stores its FP32 sums, and a reduction adds the splits in order and
+//     rounds once to bf16.
 //
 // Tiling. A workgroup of 4 waves owns a BM x 256 output tile of one expert's rows (row
 // tiles come from the dispatch tile list; an expert's group is padded to BM rows).
@@ -153,6 +156,7 @@ struct Cfg {
     static_assert(MODE != 1 || WAVES_N * (FN / 2) == 8, "gate/up pairing");
     static_assert(MODE != 1 || 4 * WAVES_N * BM <= STAGE_BYTES, "epilogue fits a slot");
     static_assert(MODE == 1 || FN == 8 || FN == 4, "one 16- or 8-byte store per row");
+    static_assert(MODE != 4 || BM <= 128, "split-K runs without the tail split");
 };
 
 template <int BM, int WAVES_M, int WAVES_N, int MODE>
@@ -181,10 +185,15 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
     // any time share A rows and B columns in its L2. With the tail split, the tiles of a
     // last round that would be at most half full are left to the tail launch, which runs
     // each of them as two 128-row halves (workgroup u: tile main_total + u/2, half u%2).
-    int num_mt = args.meta[0];
+    // A dense plain GEMM (dense_rows > 0) needs no row or tile list: tile mt is rows
+    // mt*hblk .. mt*hblk+hblk-1 of group 0 (hblk = the launch's tile rows, which the tail
+    // launch runs as two halves), and rows at or past dense_rows are padding
+    const bool dense = MODE >= 3 && args.dense_rows > 0;
+    int num_mt = dense ? (args.dense_rows + args.hblk - 1) / args.hblk : args.meta[0];
     if (num_mt > args.max_tiles) num_mt = args.max_tiles;
     const int NT = args.n_tiles;
-    const int total = num_mt * NT;
+    const int S = MODE == 4 ? args.splits : 1;   // split-K: S workgroups per output tile
+    const int total = num_mt * NT * S;
     int main_total = total;
     if (args.split_round > 0) {
         const int rem = total % args.split_round;
@@ -203,15 +212,20 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
         v = main_total + (u >> 1);
         half = u & 1;
     }
+    const int split = MODE == 4 ? v % S : 0;
+    if (MODE == 4) v /= S;
     const int grp = v / (kGroupM * NT);
     const int mt0 = grp * kGroupM;
     const int gm = min(kGroupM, num_mt - mt0);
     const int vin = v - grp * kGroupM * NT;
     const int mt = mt0 + vin % gm;
     const int nt = vin / gm;
-    const int expert = args.tile_expert[mt];
-    const int row0 = args.tile_row0[mt] + half * BM;
-    const int nks = args.K / kBK;              // >= 2
+    const int expert = dense ? 0 : args.tile_expert[mt];
+    const int row0 = (dense ? mt * args.hblk : args.tile_row0[mt]) + half * BM;
+    // K steps of this workgroup: all of them, or (split-K) the split's range, which starts at
+    // a multiple of 4 so that scale words and byte selects line up
+    const int k_begin = MODE == 4 ? split * args.ks_split : 0;
+    const int nks = MODE == 4 ? min(args.ks_split, args.K / kBK - k_begin) : args.K / kBK;   // >= 2
 
     // ---- A rows this lane fetches and reads scales for ----------------------------------
     // Every tile load and scale load is a buffer load: 32-bit per-lane offset in a VGPR,
@@ -228,6 +242,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
     const int NKB = args.K / kBK;
     const uint32_t a_kstep = blocked ? (uint32_t)args.hblk * kBK : (uint32_t)kBK;
     auto src_row = [&](int r) __attribute__((always_inline)) -> uint32_t {
+        if (dense) return row0 + r < args.dense_rows ? (uint32_t)(row0 + r) : 0u;
         const int slot = args.perm[row0 + r];
         if (slot < 0) return 0u;
         return MODE == 3 ? (uint32_t)slot : (uint32_t)(slot / args.topk);
@@ -241,14 +256,15 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
                                      (uint32_t)(row0 % args.hblk + r);
             a_off[j] = blk_row * kBK + a_chunk * 16;
         } else {
-            a_off[j] = src_row(r) * (uint32_t)args.a_stride + a_chunk * 16;
+            a_off[j] = src_row(r) * (uint32_t)args.a_stride + a_chunk * 16 + (uint32_t)(k_begin * kBK);
         }
     }
     uint32_t sa_off[FM];
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
         const int r = wm * WM + fm * 16 + (lane & 15);
-        sa_off[fm] = (blocked ? (uint32_t)(row0 + r) : src_row(r)) * (uint32_t)args.a_sf_stride;
+        sa_off[fm] = (blocked ? (uint32_t)(row0 + r) : src_row(r)) * (uint32_t)args.a_sf_stride +
+                     (uint32_t)k_begin;   // byte of scale block k_begin (k_begin % 4 == 0)
     }
     // B fragment index of the wave's n-th fragment
     auto bfrag = [&](int fn) __attribute__((always_inline)) -> int {
@@ -258,9 +274,12 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
     const __amdgpu_buffer_rsrc_t rs_a = __builtin_amdgcn_make_buffer_rsrc((void*)args.a, 0, kAllRecords, kRsrcWord3);
     const __amdgpu_buffer_rsrc_t rs_asf = __builtin_amdgcn_make_buffer_rsrc((void*)args.a_sf, 0, kAllRecords, kRsrcWord3);
     const __amdgpu_buffer_rsrc_t rs_b = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(args.b + (size_t)expert * args.b_expert + (size_t)nt * args.b_ntile), 0, kAllRecords, kRsrcWord3);
+        (void*)(args.b + (size_t)expert * args.b_expert + (size_t)nt * args.b_ntile + (size_t)k_begin * kBTileBytes),
+        0, kAllRecords, kRsrcWord3);
     const __amdgpu_buffer_rsrc_t rs_bsf = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(args.b_sf + (size_t)expert * args.bs_expert + (size_t)nt * args.bs_ntile), 0, kAllRecords, kRsrcWord3);
+        (void*)(args.b_sf + (size_t)expert * args.bs_expert + (size_t)nt * args.bs_ntile +
+                (size_t)(k_begin / 4) * (kBScaleBlockBytes / 4)),
+        0, kAllRecords, kRsrcWord3);
     const uint32_t b_voff = (uint32_t)(wave * B_DMA * 1024 + lane * 16);
     const uint32_t bs_voff = (uint32_t)(lane * 4);
 
@@ -464,6 +483,25 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
                                                              row_u * (uint32_t)args.h_sf_stride + nt, 0);
                 }
             }
+        } else if constexpr (MODE == 4) {
+            // Split-K: the FP32 sums of this K range, row-major [BM][256] per (tile, split),
+            // every row of the tile (the reduction skips padding rows and columns past N).
+            // Lane column l of the wave's fragments holds columns col0 .. col0+FN-1, as below.
+            const int l = lane & 15;
+            const int fw = wn * FN;
+            const int col0 = 128 * (fw >> 3) + 8 * l + (fw & 7);
+            float* pbase = args.partial + ((size_t)((mt * NT + nt) * S + split) * BM) * kBN + col0;
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float* dst = pbase + (size_t)(wm * WM + fm * 16 + 4 * g + r) * kBN;
+#pragma unroll
+                    for (int q = 0; q < FN / 4; ++q)
+                        *reinterpret_cast<v4f*>(dst + 4 * q) = (v4f){acc[fm][4 * q][r], acc[fm][4 * q + 1][r],
+                                                                     acc[fm][4 * q + 2][r], acc[fm][4 * q + 3][r]};
+                }
+            }
         } else {
             // Lane column l of the wave's fragments wn*FN .. wn*FN+FN-1 holds output columns
             // col0 .. col0+FN-1 (the packed W2 interleaves its rows so). Each row is scaled by
@@ -482,7 +520,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) slot[fm][r] = args.perm[row0 + wm * WM + fm * 16 + 4 * g + r];
+                for (int r = 0; r < 4; ++r) {
+                    const int row = row0 + wm * WM + fm * 16 + 4 * g + r;
+                    slot[fm][r] = dense ? (row < args.dense_rows ? row : -1) : args.perm[row];
+                }
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
@@ -511,6 +552,57 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
             }
         }
 #endif
+}
+
+// Split-K reduction of the plain GEMM: thread (tile, row, 4-column chunk) adds the S FP32
+// partials of its 4 columns in split order, rounds once to bf16 (nearest even) and stores
+// them into the row of D the row list names; padding rows and columns past N are skipped.
+// The partial loads of 4 splits at a time are issued before their sums.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ partial,
+                                                            const int32_t* __restrict__ perm,
+                                                            const int32_t* __restrict__ meta,
+                                                            const int32_t* __restrict__ tile_row0,
+                                                            int max_tiles, int NT, int S, int BM, int N,
+                                                            int dense_rows, uint16_t* __restrict__ d) {
+    typedef float v2f __attribute__((ext_vector_type(2)));
+    typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+    int num_mt = dense_rows > 0 ? (dense_rows + BM - 1) / BM : meta[0];
+    if (num_mt > max_tiles) num_mt = max_tiles;
+    const size_t idx = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
+    const size_t per_tile = (size_t)BM * (kBN / 4);
+    const size_t tile = idx / per_tile;
+    if (tile >= (size_t)num_mt * NT) return;
+    const int rem = (int)(idx - tile * per_tile);
+    const int row = rem / (kBN / 4), c4 = rem % (kBN / 4);
+    const int mt = (int)(tile / NT), nt = (int)(tile % NT);
+    const int col = nt * kBN + c4 * 4;
+    if (col >= N) return;
+    int out_row;
+    if (dense_rows > 0) {
+        out_row = mt * BM + row;
+        if (out_row >= dense_rows) return;
+    } else {
+        out_row = perm[tile_row0[mt] + row];
+        if (out_row < 0) return;
+    }
+    const float* p = partial + ((tile * S) * BM + row) * kBN + c4 * 4;
+    const size_t stride = (size_t)BM * kBN;
+    v4f sum = *reinterpret_cast<const v4f*>(p);
+    int sp = 1;
+    for (; sp + 4 <= S; sp += 4) {
+        const v4f a0 = *reinterpret_cast<const v4f*>(p + sp * stride);
+        const v4f a1 = *reinterpret_cast<const v4f*>(p + (sp + 1) * stride);
+        const v4f a2 = *reinterpret_cast<const v4f*>(p + (sp + 2) * stride);
+        const v4f a3 = *reinterpret_cast<const v4f*>(p + (sp + 3) * stride);
+        sum += a0;
+        sum += a1;
+        sum += a2;
+        sum += a3;
+    }
+    for (; sp < S; ++sp) sum += *reinterpret_cast<const v4f*>(p + sp * stride);
+    const uint32_t lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(((v2f){sum.x, sum.y}), v2bf));
+    const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(((v2f){sum.z, sum.w}), v2bf));
+    *reinterpret_cast<uint2*>(d + (size_t)out_row * N + col) = make_uint2(lo, hi);
 }
 
 template <int BM, int WAVES_M, int WAVES_N, int MODE>
@@ -553,6 +645,10 @@ hipError_t launch_mode(int block_m, const GemmArgs& a, hipStream_t stream) {
             m.tail = 0;
             hipError_t e = launch_cfg<256, 2, 2, MODE>(m, stream);
             if (e != hipSuccess || m.split_round == 0) return e;
+            if (m.host_tiles >= 0) {   // tile count known on the host: launch the tail only if it has work
+                const long long rem = (long long)m.host_tiles * m.n_tiles % m.split_round;
+                if (rem == 0 || 2 * rem > m.split_round) return e;
+            }
             GemmArgs t = m;
             t.tail = 1;
             grouped_gemm_kernel<128, 2, 2, MODE><<<(unsigned)m.split_round, kThreads, 0, stream>>>(t);
@@ -584,6 +680,25 @@ hipError_t launch_linear2(int block_m, const GemmArgs& a, hipStream_t stream) {
 }
 hipError_t launch_gemm_plain(int block_m, const GemmArgs& a, hipStream_t stream) {
     return launch_mode<3>(block_m, a, stream);
+}
+hipError_t launch_gemm_splitk(int block_m, const GemmArgs& a, hipStream_t stream) {
+    if (a.max_tiles == 0 || a.n_tiles == 0) return hipSuccess;
+    GemmArgs m = a;
+    m.split_round = 0;
+    m.tail = 0;
+    const unsigned grid = (unsigned)m.max_tiles * (unsigned)m.n_tiles * (unsigned)m.splits;
+    if (block_m == 128)
+        grouped_gemm_kernel<128, 2, 2, 4><<<grid, kThreads, 0, stream>>>(m);
+    else if (block_m == 64)
+        grouped_gemm_kernel<64, 1, 4, 4><<<grid, kThreads, 0, stream>>>(m);
+    else
+        return hipErrorInvalidValue;
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    const size_t n = (size_t)m.max_tiles * m.n_tiles * block_m * (kBN / 4);
+    splitk_reduce_kernel<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(
+        m.partial, m.perm, m.meta, m.tile_row0, m.max_tiles, m.n_tiles, m.splits, block_m, m.out_cols,
+        m.dense_rows, m.stage);
+    return hipGetLastError();
 }
 
 }  // namespace moe

@@ -1,8 +1,9 @@
 // C ABI of the plain FP8 x FP4 GEMMs and the FP8 cast (include/fp8_fp4_gemm.h): argument
 // checks, workspace layout, and the launches. Host code only; the kernels are the grouped
-// GEMM of gemm.hip in its plain mode, the routing kernels of route.hip (contiguous layout:
-// rows grouped by their group id, stable in row order, each group padded to the row-tile
-// size), the layout kernel of route.hip (dense and masked layouts), and cast.hip.
+// GEMM of gemm.hip in its plain mode (dense: rows and tiles derived in the kernel, K split
+// over several workgroups when the output has few tiles), the routing kernels of route.hip
+// (contiguous layout: rows grouped by their group id, stable in row order, each group padded
+// to the row-tile size), the layout kernel of route.hip (masked layout), and cast.hip.
 #include "fp8_fp4_gemm.h"
 #include "moe_internal.h"
 
@@ -11,6 +12,12 @@ namespace {
 
 constexpr int kGemmMaxBlockM = 256;
 constexpr int kGemmMinBlockM = 64;
+// FP32 partials of the split-K dense GEMM (a fixed part of every GEMM workspace)
+constexpr size_t kSplitPartialBytes = size_t(16) << 20;
+// Split K only when the output tiles would fill fewer than this many workgroups
+constexpr int kSplitBelowTiles = 128;
+// Workgroups split-K aims for (the CUs of one MI355X)
+constexpr int kSplitTargetWorkgroups = 256;
 
 bool gemm_shape_ok(int G, int N, int K) {
     if (G < 1 || G > MOE_MAX_EXPERTS) return false;
@@ -22,7 +29,7 @@ bool gemm_shape_ok(int G, int N, int K) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 struct GemmWs {
-    size_t meta, blk, counts, offsets, perm, inv, tile_expert, tile_row0, total;
+    size_t meta, blk, counts, offsets, perm, inv, tile_expert, tile_row0, partial, total;
     int max_tiles, pad_rows;
 };
 
@@ -46,6 +53,7 @@ GemmWs gemm_ws(int max_rows, int G) {
     w.inv = take(rows * sizeof(int32_t));
     w.tile_expert = take(tiles * sizeof(int32_t));
     w.tile_row0 = take(tiles * sizeof(int32_t));
+    w.partial = take(kSplitPartialBytes);
     w.total = off;
     w.max_tiles = (int)tiles;
     w.pad_rows = (int)ppad;
@@ -94,7 +102,35 @@ GemmArgs plain_args(const uint8_t* a, const uint8_t* a_sf, int N, int K, const v
     g.stage = d;
     g.topk_weights = nullptr;
     g.out_cols = N;
+    g.host_tiles = -1;
+    g.dense_rows = 0;
+    g.splits = 1;
+    g.ks_split = K / kBK;
+    g.partial = reinterpret_cast<float*>(ws + W.partial);
     return g;
+}
+
+// Split-K plan of a dense GEMM with `tiles` output tiles of BM rows: how many splits of
+// how many K steps (a multiple of 4, so every split starts on a scale word), or 1 split.
+// Every split has at least 4 steps, and the FP32 partials fit the workspace.
+void split_plan(int tiles, int BM, int K, int& splits, int& ks_split) {
+    const int nks = K / kBK;
+    splits = 1;
+    ks_split = nks;
+    if (tiles >= kSplitBelowTiles || nks % 4 != 0 || nks < 8) return;
+    int want = kSplitTargetWorkgroups / tiles;
+    const size_t per_split = (size_t)tiles * BM * kBN * sizeof(float);
+    const int fit = (int)(kSplitPartialBytes / per_split);
+    want = want < fit ? want : fit;
+    want = want < nks / 4 ? want : nks / 4;
+    if (want < 2) return;
+    ks_split = (nks + want - 1) / want;
+    ks_split = (ks_split + 3) / 4 * 4;
+    splits = (nks + ks_split - 1) / ks_split;
+    if (splits < 2) {
+        splits = 1;
+        ks_split = nks;
+    }
 }
 
 }  // namespace
@@ -142,14 +178,16 @@ int moe_fp8_fp4_gemm(uint16_t* d, const uint8_t* a, const uint8_t* a_sf, int32_t
     if (m == 0) return MOE_OK;
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     const int BM = gemm_block_m(m);
-    if (launch_gemm_layout(0, m, 1, 0, nullptr, BM, W.pad_rows,
-                           reinterpret_cast<int32_t*>(ws + W.perm),
-                           reinterpret_cast<int32_t*>(ws + W.tile_expert),
-                           reinterpret_cast<int32_t*>(ws + W.tile_row0),
-                           reinterpret_cast<int32_t*>(ws + W.meta), stream) != hipSuccess)
-        return MOE_ERR_HIP;
+    // rows are 0 .. m-1 of one group: the kernels derive tiles and rows arithmetically
     const PackedBLayout L = packed_b_layout(1, n, k);
-    const GemmArgs g = plain_args(a, a_sf, n, k, packed_b, L, ws, W, d, BM, cdiv(m, BM));
+    GemmArgs g = plain_args(a, a_sf, n, k, packed_b, L, ws, W, d, BM, cdiv(m, BM));
+    g.host_tiles = cdiv(m, BM);
+    g.dense_rows = m;
+    if (BM <= 128) {
+        split_plan(cdiv(m, BM) * L.n_tiles, BM, k, g.splits, g.ks_split);
+        if (g.splits > 1)
+            return launch_gemm_splitk(BM, g, stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+    }
     if (launch_gemm_plain(BM, g, stream) != hipSuccess) return MOE_ERR_HIP;
     return MOE_OK;
 }
@@ -200,7 +238,7 @@ int moe_m_grouped_fp8_fp4_gemm_masked(uint16_t* d, const uint8_t* a, const uint8
     if (max_m == 0) return MOE_OK;
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     const int BM = gemm_block_m(expected_m);
-    if (launch_gemm_layout(1, 0, groups, max_m, masked_m, BM, W.pad_rows,
+    if (launch_gemm_layout(groups, max_m, masked_m, BM, W.pad_rows,
                            reinterpret_cast<int32_t*>(ws + W.perm),
                            reinterpret_cast<int32_t*>(ws + W.tile_expert),
                            reinterpret_cast<int32_t*>(ws + W.tile_row0),

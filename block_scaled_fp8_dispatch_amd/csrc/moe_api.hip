@@ -197,6 +197,8 @@ static int forward_impl(uint16_t* y_bf16, const uint8_t* x_fp8, const uint8_t* x
     const int max_tiles = tiles_bound < W.pub.max_tiles ? tiles_bound : W.pub.max_tiles;
 
     GemmArgs a1{};
+    a1.host_tiles = -1;   // the tile count is known only on the device
+    a1.dense_rows = 0;
     a1.a = dispatch_copy ? ws + W.pub.xg : x_fp8;
     a1.a_sf = dispatch_copy ? ws + W.pub.xg_sf : x_sf;
     a1.a_blocked = dispatch_copy ? 1 : 0;

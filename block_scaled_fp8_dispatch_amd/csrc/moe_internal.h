@@ -72,6 +72,8 @@ struct GemmArgs {
     // each as two 128-row halves (tail = 1). 0 disables it.
     int split_round;
     int tail;
+    int host_tiles;            // M tiles in use when the host knows them (dense GEMM), else -1
+    int dense_rows;            // plain GEMM only: > 0 = dense rows 0..dense_rows-1, no row list
     // B operand: packed weights
     const uint8_t* b;
     const uint32_t* b_sf;
@@ -89,12 +91,20 @@ struct GemmArgs {
     uint16_t* stage;
     const float* topk_weights;
     int out_cols;              // = H
+    // Split-K of the plain GEMM: `splits` workgroups per output tile, each over ks_split K
+    // steps (a multiple of 4), FP32 partials [tile][split][BM][256]
+    int splits;
+    int ks_split;
+    float* partial;
 };
 
 hipError_t launch_linear1(int block_m, const GemmArgs& a, hipStream_t stream);
 hipError_t launch_linear2(int block_m, const GemmArgs& a, hipStream_t stream);
 // Plain FP8 x FP4 GEMM over a row list: D[perm[p]] = bf16(A[perm[p]] . B_g^T)
 hipError_t launch_gemm_plain(int block_m, const GemmArgs& a, hipStream_t stream);
+// The same with K split over a.splits workgroups per tile (block_m 64 or 128), then the
+// in-order reduction of the FP32 partials
+hipError_t launch_gemm_splitk(int block_m, const GemmArgs& a, hipStream_t stream);
 
 // Packed B of the plain GEMMs ([G][N][K] FP4, the W2 layout): N padded to 256-row tiles
 // with zero rows
@@ -108,13 +118,11 @@ PackedBLayout packed_b_layout(int G, int N, int K);
 hipError_t launch_pack_b(int G, int N, int K, const PackedBLayout& L, const uint8_t* b,
                          const uint8_t* b_sf, uint8_t* packed, hipStream_t stream);
 
-// Row list and tile list of the plain GEMMs without a routing pass (route.hip):
-// kind 0 = dense (G = 1, M rows), kind 1 = masked (group g's rows g*max_m + i,
-// i < clamp(masked_m[g], 0, max_m)). Each group is padded to BM rows.
-hipError_t launch_gemm_layout(int kind, int M, int G, int max_m, const int32_t* masked_m,
-                              int block_m, int pad_rows_cap, int32_t* perm,
-                              int32_t* tile_expert, int32_t* tile_row0, int32_t* meta,
-                              hipStream_t stream);
+// Row list and tile list of the masked plain GEMM without a routing pass (route.hip): group
+// g's rows g*max_m + i, i < clamp(masked_m[g], 0, max_m), each group padded to BM rows.
+hipError_t launch_gemm_layout(int G, int max_m, const int32_t* masked_m, int block_m,
+                              int pad_rows_cap, int32_t* perm, int32_t* tile_expert,
+                              int32_t* tile_row0, int32_t* meta, hipStream_t stream);
 
 // FP8 cast of bf16 rows (cast.hip)
 hipError_t launch_cast_fp8(const uint16_t* x, int rows, int cols, uint8_t* q, uint8_t* sf,

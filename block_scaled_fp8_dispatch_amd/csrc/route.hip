@@ -320,12 +320,11 @@ __global__ __launch_bounds__(256) void gather_kernel(const uint8_t* __restrict__
     }
 }
 
-// Row and tile lists of the dense and masked plain GEMMs (no routing pass: the groups'
-// rows are known by position). Every workgroup scans the groups' padded sizes (group g:
-// c_g rows, ceil(c_g / BM) tiles; dense: one group of M rows; masked: c_g =
-// clamp(masked_m[g], 0, max_m)), then writes perm for its share of padded rows: A row
-// (g * max_m + i for masked, i for dense) or -1 on padding. Workgroup 0 also writes the
-// tile list and meta[0].
+// Row and tile lists of the masked plain GEMM (no routing pass: the groups' rows are known
+// by position). Every workgroup scans the groups' padded sizes (group g: c_g =
+// clamp(masked_m[g], 0, max_m) rows, ceil(c_g / BM) tiles), then writes perm for its share
+// of padded rows: A row g * max_m + i, or -1 on padding. Workgroup 0 also writes the tile
+// list and meta[0].
 constexpr int kLayoutRows = 16384;
 
 __device__ inline int upper_group(const int* off, int G, int v) {
@@ -338,7 +337,7 @@ __device__ inline int upper_group(const int* off, int G, int v) {
     return lo;
 }
 
-__global__ __launch_bounds__(1024) void gemm_layout_kernel(int kind, int M, int G, int max_m,
+__global__ __launch_bounds__(1024) void gemm_layout_kernel(int G, int max_m,
                                                           const int32_t* __restrict__ masked_m,
                                                           int block_m, int32_t* __restrict__ perm,
                                                           int32_t* __restrict__ tile_expert,
@@ -350,12 +349,8 @@ __global__ __launch_bounds__(1024) void gemm_layout_kernel(int kind, int M, int 
     const int tid = threadIdx.x;
     int c = 0;
     if (tid < G) {
-        if (kind == 0) {
-            c = M;
-        } else {
-            c = masked_m[tid];
-            c = c < 0 ? 0 : (c > max_m ? max_m : c);
-        }
+        c = masked_m[tid];
+        c = c < 0 ? 0 : (c > max_m ? max_m : c);
     }
     const int nt = (c + block_m - 1) / block_m;
     int total = 0;
@@ -372,7 +367,7 @@ __global__ __launch_bounds__(1024) void gemm_layout_kernel(int kind, int M, int 
         const int t = p / block_m;
         const int g = upper_group(toff, G, t);
         const int i = p - toff[g] * block_m;
-        perm[p] = i < cnt[g] ? (kind == 0 ? i : g * max_m + i) : -1;
+        perm[p] = i < cnt[g] ? g * max_m + i : -1;
     }
     if (blockIdx.x == 0) {
         for (int t = tid; t < total; t += 1024) {
@@ -386,14 +381,13 @@ __global__ __launch_bounds__(1024) void gemm_layout_kernel(int kind, int M, int 
 
 }  // namespace
 
-hipError_t launch_gemm_layout(int kind, int M, int G, int max_m, const int32_t* masked_m,
-                              int block_m, int pad_rows_cap, int32_t* perm,
-                              int32_t* tile_expert, int32_t* tile_row0, int32_t* meta,
-                              hipStream_t stream) {
+hipError_t launch_gemm_layout(int G, int max_m, const int32_t* masked_m, int block_m,
+                              int pad_rows_cap, int32_t* perm, int32_t* tile_expert,
+                              int32_t* tile_row0, int32_t* meta, hipStream_t stream) {
     if (G < 1 || G > MOE_MAX_EXPERTS) return hipErrorInvalidValue;
     const int grid = pad_rows_cap > 0 ? cdiv(pad_rows_cap, kLayoutRows) : 1;
-    gemm_layout_kernel<<<grid, 1024, 0, stream>>>(kind, M, G, max_m, masked_m, block_m, perm,
-                                                  tile_expert, tile_row0, meta);
+    gemm_layout_kernel<<<grid, 1024, 0, stream>>>(G, max_m, masked_m, block_m, perm, tile_expert,
+                                                  tile_row0, meta);
     return hipGetLastError();
 }
 

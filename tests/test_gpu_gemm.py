@@ -6,7 +6,9 @@ exact arithmetic on both sides). Each GEMM output element must be the bf16 round
 value within the FP32 accumulation error bound of the exact sum (oracle
 gemm_bf16_within_bound); rows and columns that must not be written keep the poison value.
 Rows of one output are independent of the row-tile size, so the masked GEMM gives the same
-bytes whatever expected_m picks.
+bytes whatever expected_m picks. Dense GEMMs with few output tiles split K over several
+workgroups (g_split128, g_dense_decode); their sums are another FP32 order of the same
+products, inside the same bound.
 """
 import numpy as np
 import pytest
@@ -73,12 +75,15 @@ def _check_rows(d, rows, ref_rows, ref):
     GEMM_CONFIGS["g_tiny"],                                           # ragged M and N, K = 3 steps
     GemmConfig("g_mid", "dense", M=1000, N=528, K=1152),              # 256-row tiles + tail halves
     GemmConfig("g_one", "dense", M=1, N=16, K=256),                   # smallest shape
-    GEMM_CONFIGS["g_dense_decode"],
+    GemmConfig("g_split128", "dense", M=200, N=1040, K=4096),         # split K, 128-row tiles
+    GEMM_CONFIGS["g_dense_decode"],                                   # split K, 64-row tiles
 ], ids=lambda c: c.name)
 def test_dense_gemm(cfg):
     print(f"[gemm] dense {cfg}", flush=True)
     inp = make_gemm_inputs(cfg, seed=1, device="cuda")
-    d = GemmRun(inp).run()
+    run = GemmRun(inp)
+    d = run.run()
+    assert np.array_equal(run.run(), d), "two calls gave different bytes"
     ref = oracle.fp8_fp4_gemm(_host(inp.a), _host(inp.a_sf), _host(inp.b[0]), _host(inp.b_sf[0]), cfg.K)
     rows = np.arange(cfg.M)
     _check_rows(d, rows, rows, ref)
