@@ -1,8 +1,8 @@
 """GPU edge cases and exact invariants of the forward, through the C ABI.
 
 Edge cases: zero tokens, fewer tokens than the workspace capacity, every slot on one
-expert (with duplicate experts inside a token), k = E, unused (-1) and invalid expert
-ids with the diagnostic count, many experts with most of them empty.
+expert (with duplicate experts inside a token), k = E, the largest k (64), unused (-1) and
+invalid expert ids with the diagnostic count, many experts with most of them empty.
 
 Invariants that hold bit for bit on the GPU, whatever the tolerance against the oracle:
 the same call twice gives the same bytes; permuting tokens permutes y; relabelling
@@ -110,6 +110,15 @@ def test_unused_and_invalid_slots():
     invalid, counts = moe.moe_read_diagnostics(run.shape, run.ws)
     assert invalid == int(r["num_invalid"]) == int(((idx < -1) | (idx >= cfg.E)).sum())
     assert counts == [int(c) for c in r["counts"]]
+
+
+def test_largest_topk():
+    """k = 64, the most slots per token the boundary accepts (64 distinct experts per token)."""
+    cfg = MoEConfig("edge", T=40, E=80, k=64, H=256, I=256)
+    print(f"[edge] k = 64 {cfg}", flush=True)
+    inp = make_inputs(cfg, seed=18, device="cuda")
+    run = Run(inp)
+    _parity(run, inp)
 
 
 def test_many_experts_mostly_empty():

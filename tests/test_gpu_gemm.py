@@ -10,6 +10,8 @@ bytes whatever expected_m picks. Dense GEMMs with few output tiles split K over 
 workgroups (g_split128, g_dense_decode); their sums are another FP32 order of the same
 products, inside the same bound.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -148,6 +150,31 @@ def test_masked_gemm(cfg):
     for em in (1, 200, 4096):
         d2 = run.run(expected_m=em).reshape(cfg.G, cfg.M, cfg.N)
         assert np.array_equal(d2, d), f"expected_m={em} changed the output"
+
+
+def test_grouped_gemms_with_the_most_groups():
+    """1024 groups (the most the boundary accepts), most of them tiny or empty."""
+    G, N, K = 1024, 32, 256
+    cfg = GemmConfig("g_masked_1024", "masked", M=3, N=N, K=K, G=G, expected_m=1)
+    print(f"[gemm] {cfg}", flush=True)
+    inp = make_gemm_inputs(cfg, seed=6, device="cuda")
+    cnt = np.random.default_rng(1).integers(-1, 4, size=G).astype(np.int32)
+    inp.masked_m = torch.from_numpy(cnt).cuda()
+    d = GemmRun(inp).run().reshape(G, 3, N)
+    a, a_sf, b, b_sf = _host(inp.a), _host(inp.a_sf), _host(inp.b), _host(inp.b_sf)
+    ref = oracle.m_grouped_gemm_masked(a, a_sf, cnt, b, b_sf, K)
+    v = ref["valid"]
+    assert (d[~v] == POISON).all()
+    ok = oracle.gemm_bf16_within_bound(d[v], ref["exact"][v], ref["bound"][v])
+    assert ok.all(), f"{(~ok).sum()} elements off"
+    # the same rows as a contiguous layout: row (g, i) belongs to group g when i < count
+    cfg2 = GemmConfig("g_contig_1024", "contiguous", M=G * 3, N=N, K=K, G=G)
+    inp2 = dataclasses.replace(inp, cfg=cfg2, a=inp.a.reshape(G * 3, K), a_sf=inp.a_sf.reshape(G * 3, -1),
+                               masked_m=None)
+    grp = np.where(v, np.arange(G)[:, None], -1).reshape(-1).astype(np.int32)
+    inp2.group_of_row = torch.from_numpy(grp).cuda()
+    d2 = GemmRun(inp2).run().reshape(G, 3, N)
+    assert np.array_equal(d2, d), "contiguous and masked layouts of the same rows differ"
 
 
 def test_masked_gemm_graph_replays_follow_device_counts():
