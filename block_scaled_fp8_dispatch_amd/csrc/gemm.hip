@@ -3,9 +3,10 @@
 // instruction, FP32 accumulation).
 //
 //   Linear1 (chenxutan.com/d/1930 section 3.1 step 2): the dispatched rows of x (copied
-//     into expert order by the dispatch) x packed W1 of the row tile's expert; the epilogue applies
-//     SwiGLU (step 3) and requantises h to e4m3 with one UE8M0 scale per 1x128 block
-//     (section 11.1's per-block amax scaling, rounded up to a power of two).
+//     into expert order by the dispatch when k <= 2, else read from x through the row list)
+//     x packed W1 of the row tile's expert; the epilogue applies SwiGLU (step 3) and
+//     requantises h to e4m3 with one UE8M0 scale per 1x128 block (section 11.1's per-block
+//     amax scaling, rounded up to a power of two).
 //   Linear2 (step 4): rows of h8 x packed W2; the epilogue multiplies each row by its
 //     top-k weight and writes it, as bf16, to the staging row of its (token, slot) (the
 //     combine of step 5 then sums a token's slots in slot order, without atomics).
@@ -17,7 +18,9 @@
 //     rounds once to bf16.
 //
 // Tiling. A workgroup of 4 waves owns a BM x 256 output tile of one expert's rows (row
-// tiles come from the dispatch tile list; an expert's group is padded to BM rows).
+// tiles come from the dispatch tile list; an expert's group is padded to BM rows). When
+// the last round of 256-row tiles would be at most half full, a second launch runs its
+// tiles as 128-row halves.
 //
 // Pipeline. The A tile of a K step (BM x 128 bytes, XOR-swizzled 16-byte chunks) and the
 // B tile (16 packed fragments, 16 KB) are fetched straight into a 3-slot LDS ring with
