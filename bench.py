@@ -52,8 +52,17 @@ def parse():
     return ap.parse_args()
 
 
+def code_hash(text: str) -> str:
+    """sha256 (first 16 hex) of C++ source with comments and whitespace removed: a change
+    to the comments alone does not change the kernel the counters were taken on."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    text = re.sub(r"\s+", "", text)
+    return hashlib.sha256(text.encode()).hexdigest()[:16]
+
+
 def gemm_source_hash() -> str:
-    return hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()[:16]
+    return code_hash(open(GEMM_SRC, encoding="utf-8").read())
 
 
 def load_traffic(cfg_name: str):
