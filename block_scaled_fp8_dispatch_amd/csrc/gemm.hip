@@ -23,11 +23,15 @@
 // tiles as 128-row halves.
 //
 // Pipeline. The A tile of a K step (BM x 128 bytes, XOR-swizzled 16-byte chunks) and the
-// B tile (16 packed fragments, 16 KB) are fetched straight into a 3-slot LDS ring with
-// gfx950's global_load_lds_dwordx4 (no staging registers). There is one barrier per K
-// step, half way through its MFMAs: after it the loads two steps ahead are issued and the
-// next step's B fragments and first A fragment are read into registers, so MFMAs never
-// wait on LDS at a step boundary and every tile load has a full step to arrive. The steps
+// B tile (16 packed fragments, 16 KB) are fetched straight into LDS rings with gfx950's
+// global_load_lds_dwordx4 (no staging registers): A into 3 slots, loaded two steps ahead;
+// B into 4 slots, loaded three steps ahead (3 slots and two steps for 64-row tiles, whose
+// LDS must leave room for two workgroups per CU). 256-row tiles fill the CU's 160 KB. There
+// is one barrier per K step, half way through its MFMAs: it waits for this wave's loads of
+// the next step (only the B loads issued after them may stay in flight), and after it the
+// next loads are issued and the next step's B fragments and first A fragment are read into
+// registers, so MFMAs never wait on LDS at a step boundary; A loads have a step to
+// arrive, B loads two. The steps
 // are branch-free and carry scheduling-group hints, so the compiler places one load
 // between consecutive MFMAs instead of issuing the loads as a burst. Scales are read
 // straight from global memory: one 32-bit word per lane covers four K steps, and the
@@ -54,7 +58,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kGroupM = 4;
 constexpr int kThreads = 256;
-constexpr int kStages = 3;
+constexpr int kStages = 3;   // A ring slots
 // Word 3 of a raw buffer descriptor on gfx950 (32-bit data format, no swizzle); with a zero
 // stride, offsets are plain byte offsets, range-checked against the record count.
 constexpr int kRsrcWord3 = 0x00020000;
@@ -151,13 +155,18 @@ struct Cfg {
     static constexpr int FN = WN / 16;
     static constexpr int A_BYTES = BM * kBK;
     static constexpr int STAGE_BYTES = A_BYTES + kBTileBytes;
+    // B ring depth: 4 slots (B loads 3 steps ahead) where the LDS allows it; 64-row tiles
+    // keep 3 (72 KB, two workgroups per CU)
+    static constexpr int KB = BM == 64 ? 3 : 4;
+    static constexpr int DB = KB - 1;
+    static constexpr int LDS_BYTES = kStages * A_BYTES + KB * kBTileBytes;
     static constexpr int A_DMA = A_BYTES / 1024 / 4;   // 1 KB direct-to-LDS loads per wave
     static constexpr int B_DMA = kBTileBytes / 1024 / 4;
     static constexpr int DMA = A_DMA + B_DMA;
     static_assert(WAVES_M * WAVES_N == 4, "4 waves");
     static_assert(FM >= 2 && FM % 2 == 0, "mid-step split");
     static_assert(MODE != 1 || WAVES_N * (FN / 2) == 8, "gate/up pairing");
-    static_assert(MODE != 1 || 4 * WAVES_N * BM <= STAGE_BYTES, "epilogue fits a slot");
+    static_assert(MODE != 1 || 4 * WAVES_N * BM <= A_BYTES, "epilogue fits a slot");
     static_assert(MODE == 1 || FN == 8 || FN == 4, "one 16- or 8-byte store per row");
     static_assert(MODE != 4 || BM <= 128, "split-K runs without the tail split");
 };
@@ -171,8 +180,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
     constexpr int WM = C::WM, WN = C::WN, FM = C::FM, FN = C::FN;
     constexpr int A_BYTES = C::A_BYTES, STAGE_BYTES = C::STAGE_BYTES;
     constexpr int A_DMA = C::A_DMA, B_DMA = C::B_DMA, DMA = C::DMA;
+    constexpr int KB = C::KB, DB = C::DB;
 
-    __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * STAGE_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS_BYTES];
+    uint8_t* const bring = smem + kStages * A_BYTES;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -289,13 +300,14 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
     // one direct-to-LDS load (j < A_DMA: A rows, else B fragments) of K step ks into ring
     // slot `slot` (ks is clamped by the caller)
     auto dma_one = [&](int ks, int slot, int j) __attribute__((always_inline)) {
-        uint8_t* As = smem + slot * STAGE_BYTES;
         if (j < A_DMA) {
+            uint8_t* As = smem + slot * A_BYTES;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_a, MOE_LPTR(As + (wave * A_DMA + j) * 1024), 16,
                                                      a_off[j], ks * a_kstep, 0, 0);
         } else {
             const int jj = j - A_DMA;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_b, MOE_LPTR(As + A_BYTES + (wave * B_DMA + jj) * 1024),
+            uint8_t* Bs = bring + slot * kBTileBytes;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_b, MOE_LPTR(Bs + (wave * B_DMA + jj) * 1024),
                                                      16, b_voff, ks * kBTileBytes + jj * 1024, 0, 0);
         }
     };
@@ -309,15 +321,15 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
     // LDS fragment reads: per-lane base addresses; fragment and slot offsets are uniform
     const uint32_t a_lo = (uint32_t)((wm * WM + (lane & 15)) * kBK + ((g ^ (lane & 7)) << 4));
     const uint32_t a_hi = (uint32_t)((wm * WM + (lane & 15)) * kBK + (((g + 4) ^ (lane & 7)) << 4));
-    const uint32_t b_rd = (uint32_t)(A_BYTES + lane * 16);
+    const uint32_t b_rd = (uint32_t)(lane * 16);
     auto read_a = [&](int slot, int fm) __attribute__((always_inline)) -> v8i {
-        const uint8_t* As = smem + slot * STAGE_BYTES + fm * 16 * kBK;
+        const uint8_t* As = smem + slot * A_BYTES + fm * 16 * kBK;
         const v4i lo4 = *reinterpret_cast<const v4i*>(As + a_lo);
         const v4i hi4 = *reinterpret_cast<const v4i*>(As + a_hi);
         return (v8i){lo4.x, lo4.y, lo4.z, lo4.w, hi4.x, hi4.y, hi4.z, hi4.w};
     };
     auto read_b = [&](int slot, int fn) __attribute__((always_inline)) -> v4i {
-        const uint8_t* Bs = smem + slot * STAGE_BYTES + bfrag(fn) * kFragBytes;
+        const uint8_t* Bs = bring + slot * kBTileBytes + bfrag(fn) * kFragBytes;
         return *reinterpret_cast<const v4i*>(Bs + b_rd);
     };
 
@@ -335,14 +347,25 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
     // scale words of two consecutive 4-step blocks: set (ks / 4) % 2 serves step ks
     uint32_t sa[2][FM], sb[2][FN];
 
-    // prologue: K steps 0 and 1
+    // prologue, in the order the steps keep (scales, then A, then B): scales of block 0,
+    // A and B of step 0, B of steps 1 .. DB-2, A of step 1, B of step DB-1; so that at
+    // every barrier the only loads allowed in flight are the B loads issued after the A
+    // loads of the next step
+#pragma unroll
+    for (int i = 0; i < FM + FN; ++i) scale_one(0, i, sa[0], sb[0]);
 #pragma unroll
     for (int j = 0; j < DMA; ++j) dma_one(0, 0, j);
 #pragma unroll
-    for (int j = 0; j < DMA; ++j) dma_one(1, 1, j);
+    for (int s2 = 1; s2 < DB - 1; ++s2)
 #pragma unroll
-    for (int i = 0; i < FM + FN; ++i) scale_one(0, i, sa[0], sb[0]);
-    wait_vmem_barrier();
+        for (int j = A_DMA; j < DMA; ++j) dma_one(min(s2, nks - 1), s2, j);
+#pragma unroll
+    for (int j = 0; j < A_DMA; ++j) dma_one(1, 1, j);
+#pragma unroll
+    for (int j = A_DMA; j < DMA; ++j) dma_one(min(DB - 1, nks - 1), DB - 1, j);
+    constexpr int WAIT0 = (DB - 1) * B_DMA + A_DMA;          // everything after B(0)
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (WAIT0 & 15) | (((WAIT0 >> 4) & 3) << 14));
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" :: "n"(WAIT0) : "memory");
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) bq[fn] = read_b(0, fn);
     a_nx = read_a(0, 0);
@@ -350,11 +373,12 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
     // One K step, free of branches and scheduled by hand: every MFMA is followed by at most
     // a few memory operations, in a fixed order the compiler may not change (scheduling
     // barriers that only let ALU work move). Each A fragment is read right after the first
-    // MFMA of the fragment before it. Half way: barrier (this wave's loads of step ks+1 have
-    // landed, every wave is past step ks-1); in the second half, the loads of step ks+2
-    // (clamped to the last step: a harmless reload into a free slot) and, in the third step
-    // of each 4-step block, the scale words of the next block into the other scale set
-    // (needed only after the next barrier, which waits for them) go one or a few per MFMA.
+    // MFMA of the fragment before it. Half way: barrier (this wave's A and B of step ks+1
+    // have landed, every wave is past step ks-1); in the second half go, one or a few per
+    // MFMA and in this order: in the third step of each 4-step block the scale words of
+    // the next block into the other scale set (needed only after the next barrier, which
+    // waits for them), the A loads of step ks+2 and the B loads of step ks+DB (clamped to
+    // the last step: a harmless reload into a free slot).
     // The last A fragment's MFMAs reload each B fragment register with the next step's
     // fragment right after its last use, and the next step's first A fragment is read with
     // them: no double buffers.
@@ -364,13 +388,18 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
         constexpr int HALF = FM / 2 * FN;
         constexpr int NOPS = DMA + (OPS == 2 ? FM + FN : 0);
         constexpr int PER = (NOPS + HALF - 1) / HALF;
+        constexpr int NS = OPS == 2 ? FM + FN : 0;          // scale loads of this step, issued first
         const int slot = ks % kStages;
         const int slot1 = (ks + 1) % kStages;
         const int slot2 = (ks + 2) % kStages;
+        const int bslot1 = (ks + 1) % KB;
+        const int bslotn = (ks + DB) % KB;
         const int ks2 = min(ks + 2, nks - 1);
+        const int ksb = min(ks + DB, nks - 1);
         auto issue = [&](int op) __attribute__((always_inline)) {
-            if (op < DMA) dma_one(ks2, slot2, op);
-            else if (op < NOPS) scale_one(ks2, op - DMA, sa[SET ^ 1], sb[SET ^ 1]);
+            if (op < NS) scale_one(ks2, op, sa[SET ^ 1], sb[SET ^ 1]);
+            else if (op < NS + A_DMA) dma_one(ks2, slot2, op - NS);
+            else if (op < NOPS) dma_one(ksb, bslotn, op - NS);
         };
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) {
@@ -379,7 +408,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
             for (int fn = 0; fn < FN; ++fn) {
                 mfma_scaled<OPS>(acc[fm][fn], a_cur, bq[fn], sa[SET][fm], sb[SET][fn]);
                 if (fn == 0) a_nx = fm + 1 < FM ? read_a(slot, fm + 1) : read_a(slot1, 0);
-                if (fm == FM - 1) bq[fn] = read_b(slot1, fn);
+                if (fm == FM - 1) bq[fn] = read_b(bslot1, fn);
                 if (fm >= FM / 2) {
                     const int t = (fm - FM / 2) * FN + fn;
 #pragma unroll
@@ -387,7 +416,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
                 }
                 __builtin_amdgcn_sched_barrier(0x7);
             }
-            if (fm == FM / 2 - 1) wait_vmem_barrier();
+            if (fm == FM / 2 - 1) {
+                // this wave's A and B of step ks+1 have landed (only the B loads of step
+                // ks-1+DB, issued after A of step ks+1, may still be in flight when DB >= 3)
+                constexpr int WN = DB >= 3 ? B_DMA : 0;
+                __builtin_amdgcn_s_waitcnt(0x0F70 | (WN & 15) | (((WN >> 4) & 3) << 14));
+                asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" :: "n"(WN) : "memory");
+            }
         }
     };
 
@@ -413,10 +448,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
     // the last steps' clamped reloads must land before the slot is reused or the wave ends
     wait_vmem_barrier();
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");   // last MFMA -> reads of acc
-    const int gs = nks;   // the epilogue uses slot (gs - 1) % 3, the last step's
-
-        // ---- epilogue, in the LDS slot of the last K step -------------------------------
-        uint8_t* ep = smem + ((gs + kStages - 1) % kStages) * STAGE_BYTES;
+        // ---- epilogue, in the first A slot (every load has landed) -----------------------
+        uint8_t* ep = smem;
         if constexpr (MODE == 1) {
             // Lane column l of the wave's gate fragment wn*FQ + q holds h column
             // col0 + q (the packed W1 interleaves its rows so), up fragment FQ + q the matching
