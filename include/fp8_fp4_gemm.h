@@ -57,12 +57,16 @@ int moe_gemm_prepare_b(int32_t groups, int32_t n, int32_t k, const uint8_t* b,
 
 /* Workspace bytes of a GEMM call whose A has up to `max_rows` rows in `groups` groups
  * (dense: m rows, 1 group; contiguous: m rows; masked: groups * max_m rows). Holds the row
- * list and tile list of the call. 0 if unsupported. */
+ * list and tile list of the call and a fixed 16 MiB area for the FP32 partial sums of a
+ * dense GEMM whose K is split over several workgroups (used when its output has fewer than
+ * 128 tiles of up to 128 x 256; the split sums are added in a fixed order, so results are
+ * deterministic). 0 if unsupported. The contents need no initialisation. */
 size_t moe_gemm_workspace_bytes(int32_t max_rows, int32_t groups);
 
 /* Dense GEMM: d[r, :] = bf16(A[r, :] . B^T) for r < m, with B = packed group 0.
  *   d     u16 [m][n] bf16 out (row stride n)
  *   a     u8 [m][k] e4m3;  a_sf  u8 [m][4*ceil(k/512)]
+ * Decode-sized outputs split K over several workgroups (see moe_gemm_workspace_bytes).
  * m = 0 launches nothing and returns MOE_OK. */
 int moe_fp8_fp4_gemm(uint16_t* d, const uint8_t* a, const uint8_t* a_sf, int32_t m, int32_t n,
                      int32_t k, const void* packed_b, void* workspace, size_t workspace_bytes,
