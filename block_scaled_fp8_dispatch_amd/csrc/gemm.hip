@@ -57,6 +57,8 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kGroupM = 4;
+// Shortest K (in elements) for which half tiles run in the second launch
+constexpr int kHalfTileMinK = 32 * kBK;
 constexpr int kThreads = 256;
 constexpr int kStages = 3;   // A ring slots
 // Word 3 of a raw buffer descriptor on gfx950 (32-bit data format, no swizzle); with a zero
@@ -196,24 +198,32 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
     // Tile ids walk groups of kGroupM row tiles across all column tiles. Workgroups go
     // round-robin to the 8 XCDs (id mod 8); each XCD owns a contiguous range of tile ids and
     // its workgroups take consecutive ids in each round, so the tiles resident on one XCD at
-    // any time share A rows and B columns in its L2. With the tail split, the tiles of a
-    // last round that would be at most half full are left to the tail launch, which runs
-    // each of them as two 128-row halves (workgroup u: tile main_total + u/2, half u%2).
+    // any time share A rows and B columns in its L2. The first launch runs the full row
+    // tiles (the tile list's first meta[3]; all tiles where half tiles are not deferred,
+    // below). With the tail split, the tiles of a last round that would be at most half full
+    // are left to the second (128-row) launch, which runs each of them as two 128-row halves
+    // (workgroup u: tile main_total + u/2, half u%2), and then each half tile (an expert's
+    // last tile holding at most 128 rows, listed after the full tiles) as one 128-row tile.
     // A dense plain GEMM (dense_rows > 0) needs no row or tile list: tile mt is rows
     // mt*hblk .. mt*hblk+hblk-1 of group 0 (hblk = the launch's tile rows, which the tail
     // launch runs as two halves), and rows at or past dense_rows are padding
     const bool dense = MODE >= 3 && args.dense_rows > 0;
     int num_mt = dense ? (args.dense_rows + args.hblk - 1) / args.hblk : args.meta[0];
     if (num_mt > args.max_tiles) num_mt = args.max_tiles;
+    // Half tiles go to the second launch only where K is long: there a 128-row tile takes
+    // about 0.6 of a 256-row tile's time; with short K the fixed costs of a tile dominate and
+    // they stay in the first launch as ordinary 256-row tiles (both launches decide alike).
+    const bool defer_half = !dense && args.K >= kHalfTileMinK;
+    const int n_full = defer_half ? min(args.meta[3], num_mt) : num_mt;
     const int NT = args.n_tiles;
     const int S = MODE == 4 ? args.splits : 1;   // split-K: S workgroups per output tile
-    const int total = num_mt * NT * S;
+    const int total = n_full * NT * S;
     int main_total = total;
     if (args.split_round > 0) {
         const int rem = total % args.split_round;
         if (rem > 0 && 2 * rem <= args.split_round) main_total = total - rem;
     }
-    int v, half = 0;
+    int v = -1, half = 0, mt, nt;
     if (!args.tail) {
         const int xcd = blockIdx.x & 7;
         const int li = blockIdx.x >> 3;
@@ -222,18 +232,27 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
         v = xcd * per + (xcd < rem ? xcd : rem) + li;
     } else {
         const int u = blockIdx.x;
-        if (u >= 2 * (total - main_total)) return;
-        v = main_total + (u >> 1);
-        half = u & 1;
+        const int halves = 2 * (total - main_total);
+        if (u < halves) {
+            v = main_total + (u >> 1);
+            half = u & 1;
+        } else {
+            const int q = u - halves;                  // half tile n_full + q / NT
+            mt = n_full + q / NT;
+            nt = q % NT;
+            if (mt >= num_mt) return;
+        }
     }
-    const int split = MODE == 4 ? v % S : 0;
-    if (MODE == 4) v /= S;
-    const int grp = v / (kGroupM * NT);
-    const int mt0 = grp * kGroupM;
-    const int gm = min(kGroupM, num_mt - mt0);
-    const int vin = v - grp * kGroupM * NT;
-    const int mt = mt0 + vin % gm;
-    const int nt = vin / gm;
+    const int split = MODE == 4 && v >= 0 ? v % S : 0;
+    if (v >= 0) {
+        if (MODE == 4) v /= S;
+        const int grp = v / (kGroupM * NT);
+        const int mt0 = grp * kGroupM;
+        const int gm = min(kGroupM, n_full - mt0);
+        const int vin = v - grp * kGroupM * NT;
+        mt = mt0 + vin % gm;
+        nt = vin / gm;
+    }
     const int expert = dense ? 0 : args.tile_expert[mt];
     const int row0 = (dense ? mt * args.hblk : args.tile_row0[mt]) + half * BM;
     // K steps of this workgroup: all of them, or (split-K) the split's range, which starts at
@@ -680,14 +699,16 @@ hipError_t launch_mode(int block_m, const GemmArgs& a, hipStream_t stream) {
             m.split_round = resident_workgroups<256, 2, 2, MODE>();
             m.tail = 0;
             hipError_t e = launch_cfg<256, 2, 2, MODE>(m, stream);
-            if (e != hipSuccess || m.split_round == 0) return e;
-            if (m.host_tiles >= 0) {   // tile count known on the host: launch the tail only if it has work
+            if (e != hipSuccess || (m.split_round == 0 && m.max_half == 0)) return e;
+            if (m.host_tiles >= 0 && m.max_half == 0) {   // tiles known on the host: launch the tail only if it has work
                 const long long rem = (long long)m.host_tiles * m.n_tiles % m.split_round;
                 if (rem == 0 || 2 * rem > m.split_round) return e;
             }
             GemmArgs t = m;
             t.tail = 1;
-            grouped_gemm_kernel<128, 2, 2, MODE><<<(unsigned)m.split_round, kThreads, 0, stream>>>(t);
+            // leftover halves (at most split_round) and the half tiles (at most one per group)
+            const unsigned grid = (unsigned)m.split_round + (unsigned)m.max_half * (unsigned)m.n_tiles;
+            grouped_gemm_kernel<128, 2, 2, MODE><<<grid, kThreads, 0, stream>>>(t);
             return hipGetLastError();
         }
         case 128: {

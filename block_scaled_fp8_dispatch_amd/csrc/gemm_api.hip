@@ -103,6 +103,7 @@ GemmArgs plain_args(const uint8_t* a, const uint8_t* a_sf, int N, int K, const v
     g.topk_weights = nullptr;
     g.out_cols = N;
     g.host_tiles = -1;
+    g.max_half = 0;
     g.dense_rows = 0;
     g.splits = 1;
     g.ks_split = K / kBK;
@@ -215,7 +216,8 @@ int moe_m_grouped_fp8_fp4_gemm_contiguous(uint16_t* d, const uint8_t* a, const u
                      i32(W.tile_row0), W.max_tiles, stream) != hipSuccess)
         return MOE_ERR_HIP;
     const PackedBLayout L = packed_b_layout(groups, n, k);
-    const GemmArgs g = plain_args(a, a_sf, n, k, packed_b, L, ws, W, d, BM, cdiv(m, BM) + groups);
+    GemmArgs g = plain_args(a, a_sf, n, k, packed_b, L, ws, W, d, BM, cdiv(m, BM) + groups);
+    g.max_half = groups;   // the routing may list one half tile per group
     if (launch_gemm_plain(BM, g, stream) != hipSuccess) return MOE_ERR_HIP;
     return MOE_OK;
 }

@@ -198,6 +198,7 @@ static int forward_impl(uint16_t* y_bf16, const uint8_t* x_fp8, const uint8_t* x
 
     GemmArgs a1{};
     a1.host_tiles = -1;   // the tile count is known only on the device
+    a1.max_half = E;      // the routing may list one half tile per expert
     a1.dense_rows = 0;
     a1.a = dispatch_copy ? ws + W.pub.xg : x_fp8;
     a1.a_sf = dispatch_copy ? ws + W.pub.xg_sf : x_sf;

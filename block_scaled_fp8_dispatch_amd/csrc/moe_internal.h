@@ -25,6 +25,11 @@ constexpr int kBTileBytes = 16 * kFragBytes;
 // Bytes of the packed B scales of one (tile, 512-K block): 16 fragments x 64 lanes x 4.
 constexpr int kBScaleBlockBytes = 16 * 64 * 4;
 
+// Rows of a half tile: with 256-row tiles, an expert's last tile that holds at most this
+// many rows is listed after all full tiles (meta[3] = number of full tiles) and runs as one
+// 128-row tile in the second launch of the 256-row class.
+constexpr int kHalfTileRows = 128;
+
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 inline int cdiv(int a, int b) { return (a + b - 1) / b; }
 
@@ -62,7 +67,7 @@ struct GemmArgs {
     int K;                     // reduction length (multiple of 128)
     int topk;                  // a_blocked == 0: slot -> token = slot / topk
     const int32_t* perm;       // per padded row: slot (MoE) or A/D row (plain GEMM); -1 padding
-    const int32_t* meta;       // meta[0] = number of M tiles in use
+    const int32_t* meta;       // meta[0] = M tiles in use, meta[3] = full tiles among them
     const int32_t* tile_expert;
     const int32_t* tile_row0;
     int n_tiles;               // column tiles per M tile
@@ -73,6 +78,7 @@ struct GemmArgs {
     int split_round;
     int tail;
     int host_tiles;            // M tiles in use when the host knows them (dense GEMM), else -1
+    int max_half;              // most half tiles the tile list can hold (one per group), 0: none
     int dense_rows;            // plain GEMM only: > 0 = dense rows 0..dense_rows-1, no row list
     // B operand: packed weights
     const uint8_t* b;

@@ -68,6 +68,40 @@ __device__ inline void wave_match(int e, bool ok, int nbits, int lane, int& rank
     cnt = __popcll(peers);
 }
 
+// Tile list of expert e (one thread per expert, all 1024 threads of the workgroup calling):
+// its padded rows [excl, excl + pad) in tiles of block_m rows. With 256-row tiles, an
+// expert's last tile that holds at most 128 rows is a half tile: the GEMM runs it as one
+// 128-row tile in its second (128-row) launch. Half tiles go after all full tiles: full
+// tiles keep their order at index (row tile - half tiles of earlier experts), and the half
+// tile of expert e takes index n_full + (half tiles of earlier experts). meta[3] = n_full.
+// Uses warp_sums (16 ints of LDS) for its scan.
+__device__ inline void write_tile_list(int e, int E, int c, int excl, int pad, int total_rows,
+                                       int block_m, int max_tiles, int* warp_sums,
+                                       int32_t* __restrict__ tile_expert,
+                                       int32_t* __restrict__ tile_row0, int32_t* __restrict__ meta) {
+    const bool has_half = block_m == kHalfTileRows * 2 && e < E && c > 0 &&
+                          c - (pad - block_m) <= kHalfTileRows;
+    int n_half = 0;
+    __syncthreads();                                     // warp_sums may still be read
+    const int half_before = block_exclusive_scan_1024(has_half ? 1 : 0, warp_sums, &n_half);
+    const int n_full = total_rows / block_m - n_half;
+    if (e < E) {
+        const int last = has_half ? excl + pad - block_m : excl + pad;
+        for (int r = excl; r < last; r += block_m) {
+            const int t = r / block_m - half_before;
+            if (t < max_tiles) {
+                tile_expert[t] = e;
+                tile_row0[t] = r;
+            }
+        }
+        if (has_half && n_full + half_before < max_tiles) {
+            tile_expert[n_full + half_before] = e;
+            tile_row0[n_full + half_before] = last;
+        }
+    }
+    if (threadIdx.x == 0) meta[3] = n_full;
+}
+
 __global__ __launch_bounds__(kFusedThreads) void route_fused_kernel(
     const int32_t* __restrict__ idx, int num_slots, int E, int nbits, int block_m,
     int32_t* __restrict__ meta, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
@@ -99,18 +133,12 @@ __global__ __launch_bounds__(kFusedThreads) void route_fused_kernel(
     const int pad = (c + block_m - 1) / block_m * block_m;
     int total = 0;
     const int excl = block_exclusive_scan_1024(pad, warp_sums, &total);
+    write_tile_list(tid, E, c, excl, pad, total, block_m, max_tiles, warp_sums, tile_expert, tile_row0, meta);
     if (tid < E) {
         counts[tid] = c;
         offsets[tid] = excl;
         if (tid == E - 1) offsets[E] = excl + pad;
         for (int r = excl + c; r < excl + pad; ++r) perm[r] = -1;
-        for (int r = excl; r < excl + pad; r += block_m) {
-            const int t = r / block_m;
-            if (t < max_tiles) {
-                tile_expert[t] = tid;
-                tile_row0[t] = r;
-            }
-        }
         hist[tid] = excl;                                // next row of expert tid
     }
     if (tid == 0) {
@@ -181,7 +209,6 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(
     int block_m, int32_t* __restrict__ meta, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ tile_expert,
     int32_t* __restrict__ tile_row0, int max_tiles) {
-    __shared__ int padded[1024];
     __shared__ int warp_sums[16];
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -207,26 +234,18 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(
     int wave_base = 0;
     for (int w = 0; w < wave; ++w) wave_base += warp_sums[w];
     const int excl = wave_base + incl - pad;
-    padded[tid] = excl;
-    __syncthreads();
+    int total = 0;
+    for (int w = 0; w < 16; ++w) total += warp_sums[w];
+    write_tile_list(tid, E, c, excl, pad, total, block_m, max_tiles, warp_sums, tile_expert, tile_row0, meta);
     if (tid < E) {
         counts[tid] = c;
         offsets[tid] = excl;
         if (tid == E - 1) offsets[E] = excl + pad;
         for (int r = excl + c; r < excl + pad; ++r) perm[r] = -1;
-        for (int r = excl; r < excl + pad; r += block_m) {
-            const int t = r / block_m;
-            if (t < max_tiles) {
-                tile_expert[t] = tid;
-                tile_row0[t] = r;
-            }
-        }
     }
     if (tid == 0) {
         int inv = 0;
         for (int b = 0; b < nblk; ++b) inv += blk_invalid[b];
-        int total = 0;
-        for (int w = 0; w < 16; ++w) total += warp_sums[w];
         meta[0] = total / block_m;
         meta[1] = inv;
         meta[2] = block_m;
@@ -380,7 +399,10 @@ __global__ __launch_bounds__(1024) void gemm_layout_kernel(int G, int max_m,
             tile_expert[t] = g;
             tile_row0[t] = t * block_m;
         }
-        if (tid == 0) meta[0] = total;
+        if (tid == 0) {
+            meta[0] = total;
+            meta[3] = total;                             // no half tiles
+        }
     }
 }
 

@@ -126,7 +126,9 @@ int moe_forward_events(uint16_t* y_bf16,
 typedef struct {
     int32_t block_m;        /* rows per tile (the padding granularity) used for T */
     int32_t max_tiles;      /* capacity of the tile list */
-    size_t meta;            /* i32[8]: [0] tiles used, [1] invalid ids, [2] block_m */
+    size_t meta;            /* i32[8]: [0] tiles used, [1] invalid ids, [2] block_m, [3] full
+                               tiles: with block_m 256, an expert's last tile holding at most
+                               128 rows is listed after all full tiles (run as a 128-row tile) */
     size_t counts;          /* i32[E]      rows per expert */
     size_t offsets;         /* i32[E+1]    padded group starts */
     size_t perm;            /* i32[P_pad]  slot t*k+j per row, -1 on padding */

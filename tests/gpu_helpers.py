@@ -77,10 +77,40 @@ class Run:
         return h8, hs
 
 
+HALF_TILE_ROWS = 128
+
+
+def scheduled_tile_list(ref: dict, block_m: int):
+    """The order in which the GEMMs take the oracle's tiles (one per block_m padded rows of
+    an expert, in row order). With 256-row tiles, an expert's last tile that holds at most
+    128 rows is a half tile, run as one 128-row tile after every full tile: full tiles keep
+    their order, then the half tiles in expert order. The set of tiles is the oracle's; only
+    this order is a scheduling choice. Returns (tile_expert, tile_row0, number of full tiles)."""
+    te, tr = ref["tile_expert"], ref["tile_row0"]
+    if block_m != 2 * HALF_TILE_ROWS:
+        return te, tr, len(te)
+    counts, offsets = ref["counts"], ref["offsets"]
+    half = set()
+    for e, c in enumerate(counts):
+        if c == 0:
+            continue
+        pad = -(-int(c) // block_m) * block_m
+        if c - (pad - block_m) <= HALF_TILE_ROWS:
+            half.add(int(offsets[e]) + pad - block_m)
+    full = [i for i in range(len(te)) if int(tr[i]) not in half]
+    halves = [i for i in range(len(te)) if int(tr[i]) in half]
+    order = np.array(full + halves, dtype=np.int64)
+    return te[order], tr[order], len(full)
+
+
 def check_routing(got: dict, idx_np: np.ndarray, E: int):
     ref = oracle.route(idx_np, E, got["block_m"])
-    for key in ("counts", "offsets", "perm", "inv", "tile_expert", "tile_row0"):
+    for key in ("counts", "offsets", "perm", "inv"):
         assert np.array_equal(got[key], ref[key]), f"routing field {key} differs"
+    te, tr, n_full = scheduled_tile_list(ref, got["block_m"])
+    assert np.array_equal(got["tile_expert"], te), "tile list (experts) differs"
+    assert np.array_equal(got["tile_row0"], tr), "tile list (first rows) differs"
+    assert int(got["meta"][3]) == n_full, "number of full tiles differs"
     assert int(got["num_invalid"]) == int(ref["num_invalid"])
     return ref
 
