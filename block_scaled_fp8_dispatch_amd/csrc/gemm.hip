@@ -73,7 +73,6 @@ struct IntC {
     static constexpr int value = N;
 };
 
-#define MOE_GPTR(p) ((__attribute__((address_space(1))) void*)(p))
 #define MOE_LPTR(p) ((__attribute__((address_space(3))) void*)(p))
 
 // Wait for this wave's outstanding vector-memory operations (the direct-to-LDS tile loads
@@ -87,9 +86,6 @@ __device__ inline void wait_vmem_barrier() {
 }
 // Wait for this wave's LDS accesses, then meet the other waves.
 __device__ inline void wait_lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-// Meet the other waves (every LDS value this wave read has already been consumed).
-__device__ inline void plain_barrier() { asm volatile("s_barrier" ::: "memory"); }
-__device__ inline void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // UE8M0 byte for a block whose largest magnitude is `amax` (fp32): the smallest s with
 // amax <= 448 * 2^s, stored as s + 127 and clamped at 0; amax == 0 gives 127. Branch-free.
@@ -156,7 +152,6 @@ struct Cfg {
     static constexpr int FM = WM / 16;
     static constexpr int FN = WN / 16;
     static constexpr int A_BYTES = BM * kBK;
-    static constexpr int STAGE_BYTES = A_BYTES + kBTileBytes;
     // B ring depth: 4 slots (B loads 3 steps ahead) where the LDS allows it; 64-row tiles
     // keep 3 (72 KB, two workgroups per CU)
     static constexpr int KB = BM == 64 ? 3 : 4;
@@ -180,7 +175,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
 #if defined(__HIP_DEVICE_COMPILE__)
     using C = Cfg<BM, WAVES_M, WAVES_N, MODE>;
     constexpr int WM = C::WM, WN = C::WN, FM = C::FM, FN = C::FN;
-    constexpr int A_BYTES = C::A_BYTES, STAGE_BYTES = C::STAGE_BYTES;
+    constexpr int A_BYTES = C::A_BYTES;
     constexpr int A_DMA = C::A_DMA, B_DMA = C::B_DMA, DMA = C::DMA;
     constexpr int KB = C::KB, DB = C::DB;
 
