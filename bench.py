@@ -306,6 +306,7 @@ def main():
     ms = total_ms / K
     stage = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(4)] for i in range(K)])
     st_ms = stage.mean(axis=0)
+    per_step = np.array([evs[i][0].elapsed_time(evs[i][4]) for i in range(K)])   # first to last stage event
     yv = y.view(torch.bfloat16).float()
     assert torch.isfinite(yv).all().item(), "non-finite output"
 
@@ -339,7 +340,9 @@ def main():
         "stage_ms": {"dispatch": round(float(st_ms[0]), 4), "linear1": round(float(st_ms[1]), 4),
                      "linear2": round(float(st_ms[2]), 4), "combine": round(float(st_ms[3]), 4)},
         "wall_s_timed": round(wall, 3),
-        "roofline": {"bound": "mfma", "kernel": "Linear1 grouped GEMM with SwiGLU/requant epilogue (main + tail launch)",
+        "step_ms_p50": round(float(np.percentile(per_step, 50)), 4),
+        "step_ms_p99": round(float(np.percentile(per_step, 99)), 4),
+        "roofline": {"bound": "mfma", "kernel": "Linear1 grouped GEMM with SwiGLU/requant epilogue (main + second launch)",
                      "achieved": round(l1_tflops, 2), "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(l1_tflops / PEAK_TFLOPS, 4), "traffic": traffic},
         "cpu_baseline": None,
