@@ -28,11 +28,11 @@
 // B into 4 slots, loaded three steps ahead (3 slots and two steps for 64-row tiles, whose
 // LDS must leave room for two workgroups per CU). 256-row tiles fill the CU's 160 KB. There
 // is one barrier per K step, half way through its MFMAs: it waits for this wave's loads of
-// the next step (only the B loads issued after them may stay in flight), and after it the
-// next loads are issued and the next step's B fragments and first A fragment are read into
-// registers, so MFMAs never wait on LDS at a step boundary; A loads have a step to
-// arrive, B loads two. The steps
-// are branch-free and carry scheduling-group hints, so the compiler places one load
+// the next step (only the B loads issued after them may stay in flight). B loads go out in
+// the first half of a step and A loads in the second, so each has between half a step and
+// a step and a half to arrive; after the barrier the next step's B fragments and first A
+// fragment are read into registers, so MFMAs never wait on LDS at a step boundary. The
+// steps are branch-free and carry scheduling-group hints, so the compiler places one load
 // between consecutive MFMAs instead of issuing the loads as a burst. Scales are read
 // straight from global memory: one 32-bit word per lane covers four K steps, and the
 // instruction's byte select picks the step.
@@ -361,22 +361,19 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
     // scale words of two consecutive 4-step blocks: set (ks / 4) % 2 serves step ks
     uint32_t sa[2][FM], sb[2][FN];
 
-    // prologue, in the order the steps keep (scales, then A, then B): scales of block 0,
-    // A and B of step 0, B of steps 1 .. DB-2, A of step 1, B of step DB-1; so that at
-    // every barrier the only loads allowed in flight are the B loads issued after the A
-    // loads of the next step
+    // prologue, in the order the steps keep (B, then scales and A): scales of block 0, A
+    // and B of step 0, B of steps 1 .. DB-1, A of step 1; so that at every barrier the
+    // only loads allowed in flight are the B loads issued after the A loads of the next step
 #pragma unroll
     for (int i = 0; i < FM + FN; ++i) scale_one(0, i, sa[0], sb[0]);
 #pragma unroll
     for (int j = 0; j < DMA; ++j) dma_one(0, 0, j);
 #pragma unroll
-    for (int s2 = 1; s2 < DB - 1; ++s2)
+    for (int s2 = 1; s2 < DB; ++s2)
 #pragma unroll
         for (int j = A_DMA; j < DMA; ++j) dma_one(min(s2, nks - 1), s2, j);
 #pragma unroll
     for (int j = 0; j < A_DMA; ++j) dma_one(1, 1, j);
-#pragma unroll
-    for (int j = A_DMA; j < DMA; ++j) dma_one(min(DB - 1, nks - 1), DB - 1, j);
     constexpr int WAIT0 = (DB - 1) * B_DMA + A_DMA;          // everything after B(0)
     __builtin_amdgcn_s_waitcnt(0x0F70 | (WAIT0 & 15) | (((WAIT0 >> 4) & 3) << 14));
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" :: "n"(WAIT0) : "memory");
@@ -387,12 +384,17 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
     // One K step, free of branches and scheduled by hand: every MFMA is followed by at most
     // a few memory operations, in a fixed order the compiler may not change (scheduling
     // barriers that only let ALU work move). Each A fragment is read right after the first
-    // MFMA of the fragment before it. Half way: barrier (this wave's A and B of step ks+1
-    // have landed, every wave is past step ks-1); in the second half go, one or a few per
-    // MFMA and in this order: in the third step of each 4-step block the scale words of
-    // the next block into the other scale set (needed only after the next barrier, which
-    // waits for them), the A loads of step ks+2 and the B loads of step ks+DB (clamped to
-    // the last step: a harmless reload into a free slot).
+    // MFMA of the fragment before it. In the first half go the B loads of step ks+DB, one
+    // per MFMA, into the slot of step ks-1 (every wave holds that step's B fragments in
+    // registers since before the previous barrier). Half way: barrier (this wave's A and
+    // B of step ks+1 have landed, every wave is past step ks-1; the B loads just issued
+    // stay in flight). In the second half go, one or a few per MFMA: in the third step of
+    // each 4-step block the scale words of the next block into the other scale set (needed
+    // only after the next barrier, which waits for them), then the A loads of step ks+2
+    // into the slot of step ks-1. Steps past the last are clamped to it: a harmless reload
+    // into a free slot. Splitting the loads over both halves keeps the texture-address
+    // queue short; vector-memory counts retire in issue order, so a B load issued before
+    // the A loads of a step waits with them.
     // The last A fragment's MFMAs reload each B fragment register with the next step's
     // fragment right after its last use, and the next step's first A fragment is read with
     // them: no double buffers.
@@ -400,9 +402,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
         constexpr int OPS = decltype(ops_c)::value;
         constexpr int SET = decltype(set_c)::value;
         constexpr int HALF = FM / 2 * FN;
-        constexpr int NOPS = DMA + (OPS == 2 ? FM + FN : 0);
+        constexpr int NS = OPS == 2 ? FM + FN : 0;          // scale loads of this step
+        constexpr int NOPS = NS + A_DMA;                     // second-half loads
         constexpr int PER = (NOPS + HALF - 1) / HALF;
-        constexpr int NS = OPS == 2 ? FM + FN : 0;          // scale loads of this step, issued first
+        constexpr int PERB = (B_DMA + HALF - 1) / HALF;      // first-half loads
         const int slot = ks % kStages;
         const int slot1 = (ks + 1) % kStages;
         const int slot2 = (ks + 2) % kStages;
@@ -412,8 +415,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
         const int ksb = min(ks + DB, nks - 1);
         auto issue = [&](int op) __attribute__((always_inline)) {
             if (op < NS) scale_one(ks2, op, sa[SET ^ 1], sb[SET ^ 1]);
-            else if (op < NS + A_DMA) dma_one(ks2, slot2, op - NS);
-            else if (op < NOPS) dma_one(ksb, bslotn, op - NS);
+            else if (op < NOPS) dma_one(ks2, slot2, op - NS);
         };
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) {
@@ -427,13 +429,18 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
                     const int t = (fm - FM / 2) * FN + fn;
 #pragma unroll
                     for (int q = 0; q < PER; ++q) issue(t * PER + q);
+                } else {
+                    const int t = fm * FN + fn;
+#pragma unroll
+                    for (int q = 0; q < PERB; ++q)
+                        if (t * PERB + q < B_DMA) dma_one(ksb, bslotn, A_DMA + t * PERB + q);
                 }
                 __builtin_amdgcn_sched_barrier(0x7);
             }
             if (fm == FM / 2 - 1) {
                 // this wave's A and B of step ks+1 have landed (only the B loads of step
-                // ks-1+DB, issued after A of step ks+1, may still be in flight when DB >= 3)
-                constexpr int WN = DB >= 3 ? B_DMA : 0;
+                // ks+DB, issued after A of step ks+1, may still be in flight)
+                constexpr int WN = B_DMA;
                 __builtin_amdgcn_s_waitcnt(0x0F70 | (WN & 15) | (((WN >> 4) & 3) << 14));
                 asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" :: "n"(WN) : "memory");
             }
