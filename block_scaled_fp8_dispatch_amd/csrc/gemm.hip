@@ -168,7 +168,10 @@ struct Cfg {
     static_assert(MODE != 4 || BM <= 128, "split-K runs without the tail split");
 };
 
-template <int BM, int WAVES_M, int WAVES_N, int MODE>
+// ABLK: A in the blocked layout (Linear2's h8, Linear1's dispatch copy); otherwise A rows are
+// read through the row list. The forward's GEMMs (MODE 1, 2) read A's scales from the blocked
+// scale copy (h_sf, xg_sf); the plain GEMMs read them row by row.
+template <int BM, int WAVES_M, int WAVES_N, int MODE, bool ABLK>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args) {
     // The body uses gfx950 buffer descriptors, a device-only type: the host pass of the
     // split compilation sees an empty kernel and emits only its launch stub.
@@ -263,10 +266,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
     const int a_chunk = (lane & 7) ^ (lane >> 3);
     // A blocked (h8 for Linear2, the dispatched x for Linear1): row r of the tile at K step
     // ks sits at (tile block + ks) * hblk * 128 + (row in block) * 128, the per-step part in
-    // the uniform offset, and its scale row is the padded row. Otherwise (Linear1 without a
-    // dispatch copy) A is x itself, row-major, its rows the tokens perm names (padding rows
-    // read token 0 and are never stored); in the plain GEMM perm names A rows directly.
-    const bool blocked = MODE == 2 || (MODE == 1 && args.a_blocked != 0);
+    // the uniform offset. Otherwise (Linear1 without a dispatch copy) A is x itself,
+    // row-major, its rows the tokens perm names (padding rows read token 0 and are never
+    // stored); in the plain GEMM perm names A rows directly.
+    constexpr bool blocked = ABLK;
+    static_assert(!ABLK || MODE <= 2, "blocked A: the forward's GEMMs only");
+    constexpr bool sblk = MODE <= 2;   // A scales in the blocked scale layout
+    static_assert(!sblk || (FM % 4 == 0 && WM % 64 == 0), "scale words of 4 fragments per load");
     const int NKB = args.K / kBK;
     const uint32_t a_kstep = blocked ? (uint32_t)args.hblk * kBK : (uint32_t)kBK;
     auto src_row = [&](int r) __attribute__((always_inline)) -> uint32_t {
@@ -279,7 +285,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
 #pragma unroll
     for (int j = 0; j < A_DMA; ++j) {
         const int r = 8 * (wave * A_DMA + j) + (lane >> 3);
-        if (blocked) {
+        if constexpr (blocked) {
             const uint32_t blk_row = (uint32_t)(row0 / args.hblk) * (uint32_t)NKB * (uint32_t)args.hblk +
                                      (uint32_t)(row0 % args.hblk + r);
             a_off[j] = blk_row * kBK + a_chunk * 16;
@@ -287,13 +293,24 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
             a_off[j] = src_row(r) * (uint32_t)args.a_stride + a_chunk * 16 + (uint32_t)(k_begin * kBK);
         }
     }
-    uint32_t sa_off[FM];
+    // A scale words: blocked, one 16-byte load per 4 fragments (rows i, 16+i, 32+i, 48+i of
+    // a 64-row group, stored together; word w of the block is w * hblk words further on);
+    // otherwise one word per fragment from the A row's scale row
+    constexpr int NSA = sblk ? FM / 4 : FM;
+    uint32_t sa_off[NSA];
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm) {
-        const int r = wm * WM + fm * 16 + (lane & 15);
-        sa_off[fm] = (blocked ? (uint32_t)(row0 + r) : src_row(r)) * (uint32_t)args.a_sf_stride +
-                     (uint32_t)k_begin;   // byte of scale block k_begin (k_begin % 4 == 0)
+    for (int i = 0; i < NSA; ++i) {
+        if constexpr (sblk) {
+            const int r = wm * WM + i * 64 + (lane & 15);
+            sa_off[i] = 4u * blocked_scale_word((uint32_t)(row0 + r), 0u, (uint32_t)args.a_sf_stride / 4u,
+                                                (uint32_t)args.hblk);
+        } else {
+            const int r = wm * WM + i * 16 + (lane & 15);
+            sa_off[i] = src_row(r) * (uint32_t)args.a_sf_stride +
+                        (uint32_t)k_begin;   // byte of scale block k_begin (k_begin % 4 == 0)
+        }
     }
+    const uint32_t sa_kstep = sblk ? 4u * (uint32_t)args.hblk : 4u;   // per scale word (4 K steps)
     // B fragment index of the wave's n-th fragment
     auto bfrag = [&](int fn) __attribute__((always_inline)) -> int {
         if (MODE == 1) return fn < FN / 2 ? wn * (FN / 2) + fn : 8 + wn * (FN / 2) + (fn - FN / 2);
@@ -325,12 +342,24 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
                                                      16, b_voff, ks * kBTileBytes + jj * 1024, 0, 0);
         }
     };
-    // one scale word (i < FM: A row block, else B fragment) of the 4-step block holding ks
+    // scale load i of the 4-step block holding ks: i < NSA the A words (4 fragments' or one
+    // fragment's), else the word of B fragment i - NSA
     auto scale_one = [&](int ks, int i, uint32_t* sa, uint32_t* sb) __attribute__((always_inline)) {
         const int kb = ks >> 2;
-        if (i < FM) sa[i] = __builtin_amdgcn_raw_buffer_load_b32(rs_asf, sa_off[i], 4 * kb, 0);
-        else sb[i - FM] = __builtin_amdgcn_raw_buffer_load_b32(rs_bsf, bs_voff + bfrag(i - FM) * 256,
+        if (i < NSA) {
+            if constexpr (sblk) {
+                const v4i w = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rs_asf, sa_off[i], kb * sa_kstep, 0));
+                sa[4 * i] = w.x;
+                sa[4 * i + 1] = w.y;
+                sa[4 * i + 2] = w.z;
+                sa[4 * i + 3] = w.w;
+            } else {
+                sa[i] = __builtin_amdgcn_raw_buffer_load_b32(rs_asf, sa_off[i], kb * sa_kstep, 0);
+            }
+        } else {
+            sb[i - NSA] = __builtin_amdgcn_raw_buffer_load_b32(rs_bsf, bs_voff + bfrag(i - NSA) * 256,
                                                                kb * kBScaleBlockBytes, 0);
+        }
     };
     // LDS fragment reads: per-lane base addresses; fragment and slot offsets are uniform
     const uint32_t a_lo = (uint32_t)((wm * WM + (lane & 15)) * kBK + ((g ^ (lane & 7)) << 4));
@@ -365,7 +394,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
     // and B of step 0, B of steps 1 .. DB-1, A of step 1; so that at every barrier the
     // only loads allowed in flight are the B loads issued after the A loads of the next step
 #pragma unroll
-    for (int i = 0; i < FM + FN; ++i) scale_one(0, i, sa[0], sb[0]);
+    for (int i = 0; i < NSA + FN; ++i) scale_one(0, i, sa[0], sb[0]);
 #pragma unroll
     for (int j = 0; j < DMA; ++j) dma_one(0, 0, j);
 #pragma unroll
@@ -402,7 +431,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
         constexpr int OPS = decltype(ops_c)::value;
         constexpr int SET = decltype(set_c)::value;
         constexpr int HALF = FM / 2 * FN;
-        constexpr int NS = OPS == 2 ? FM + FN : 0;          // scale loads of this step
+        constexpr int NS = OPS == 2 ? NSA + FN : 0;         // scale loads of this step
         constexpr int NOPS = NS + A_DMA;                     // second-half loads
         constexpr int PER = (NOPS + HALF - 1) / HALF;
         constexpr int PERB = (B_DMA + HALF - 1) / HALF;      // first-half loads
@@ -514,7 +543,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
             const uint32_t h_blk = ((uint32_t)(row0 / args.hblk) * (uint32_t)(args.h_stride / 128) + nt) *
                                    (uint32_t)args.hblk * 128u + (uint32_t)(row0 % args.hblk) * 128u;
             const uint32_t h_lane = (uint32_t)((wm * WM + 4 * g) * 128 + col0);
-            const uint32_t sf_lane = (uint32_t)((wm * WM + 4 * g) * args.h_sf_stride);
+            const uint32_t hsf_words = (uint32_t)args.h_sf_stride / 4u;   // scale words per h row
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm) {
 #pragma unroll
@@ -525,7 +554,6 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
                     for (int w = 1; w < WAVES_N; ++w) mb = max(mb, red[w * BM + rt]);
                     const int byte = requant_scale_byte(__uint_as_float(mb));
                     const float mul = __uint_as_float((uint32_t)(254 - byte) << 23);  // 2^-(byte-127)
-                    const uint32_t row_u = (uint32_t)(row0 + fm * 16 + r);
                     int pk = __builtin_amdgcn_cvt_pk_fp8_f32(acc[fm][0][r] * mul, acc[fm][1][r] * mul, 0, false);
                     if constexpr (FQ == 4) {
                         pk = __builtin_amdgcn_cvt_pk_fp8_f32(acc[fm][2][r] * mul, acc[fm][3][r] * mul, pk, true);
@@ -535,9 +563,12 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
                         __builtin_amdgcn_raw_buffer_store_b16((uint16_t)pk, rs_h8, h_lane,
                                                               h_blk + (uint32_t)(fm * 16 + r) * 128u, 0);
                     }
-                    if (wn == 0 && l == 0)
-                        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)byte, rs_hsf, sf_lane,
-                                                             row_u * (uint32_t)args.h_sf_stride + nt, 0);
+                    if (wn == 0 && l == 0)   // the scale byte of (row, block nt), blocked layout
+                        __builtin_amdgcn_raw_buffer_store_b8(
+                            (uint8_t)byte, rs_hsf,
+                            4u * blocked_scale_word((uint32_t)(row0 + rt), (uint32_t)nt >> 2, hsf_words,
+                                                    (uint32_t)args.hblk) + (uint32_t)(nt & 3),
+                            0, 0);
                 }
             }
         } else if constexpr (MODE == 4) {
@@ -662,17 +693,17 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
     *reinterpret_cast<uint2*>(d + (size_t)out_row * N + col) = make_uint2(lo, hi);
 }
 
-template <int BM, int WAVES_M, int WAVES_N, int MODE>
+template <int BM, int WAVES_M, int WAVES_N, int MODE, bool ABLK>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
     // one workgroup per possible tile; those past the tiles in use return at once
     const unsigned grid = (unsigned)a.max_tiles * (unsigned)a.n_tiles;
-    grouped_gemm_kernel<BM, WAVES_M, WAVES_N, MODE><<<grid, kThreads, 0, stream>>>(a);
+    grouped_gemm_kernel<BM, WAVES_M, WAVES_N, MODE, ABLK><<<grid, kThreads, 0, stream>>>(a);
     return hipGetLastError();
 }
 
 // Workgroups of a kernel the current device runs at once (CUs x workgroups per CU),
 // computed once per device; 0 if unknown.
-template <int BM, int WAVES_M, int WAVES_N, int MODE>
+template <int BM, int WAVES_M, int WAVES_N, int MODE, bool ABLK>
 int resident_workgroups() {
     static int cached[64] = {0};
     int dev = 0;
@@ -681,7 +712,7 @@ int resident_workgroups() {
         int cus = 0, per_cu = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &per_cu, grouped_gemm_kernel<BM, WAVES_M, WAVES_N, MODE>, kThreads, 0) != hipSuccess)
+                &per_cu, grouped_gemm_kernel<BM, WAVES_M, WAVES_N, MODE, ABLK>, kThreads, 0) != hipSuccess)
             return 0;
         cached[dev] = cus * (per_cu > 0 ? per_cu : 1);
     }
@@ -692,15 +723,15 @@ int resident_workgroups() {
 // waves of 64x128, 64 rows as 1x4 waves of 64x64. The 256-row class leaves a last round
 // that would be at most half full to a 128-row launch over tile halves (the tile count
 // is known only on the device, so that launch always goes out and finds its share).
-template <int MODE>
+template <int MODE, bool ABLK>
 hipError_t launch_mode(int block_m, const GemmArgs& a, hipStream_t stream) {
     if (a.max_tiles == 0 || a.n_tiles == 0) return hipSuccess;
     switch (block_m) {
         case 256: {
             GemmArgs m = a;
-            m.split_round = resident_workgroups<256, 2, 2, MODE>();
+            m.split_round = resident_workgroups<256, 2, 2, MODE, ABLK>();
             m.tail = 0;
-            hipError_t e = launch_cfg<256, 2, 2, MODE>(m, stream);
+            hipError_t e = launch_cfg<256, 2, 2, MODE, ABLK>(m, stream);
             if (e != hipSuccess || (m.split_round == 0 && m.max_half == 0)) return e;
             if (m.host_tiles >= 0 && m.max_half == 0) {   // tiles known on the host: launch the tail only if it has work
                 const long long rem = (long long)m.host_tiles * m.n_tiles % m.split_round;
@@ -710,20 +741,20 @@ hipError_t launch_mode(int block_m, const GemmArgs& a, hipStream_t stream) {
             t.tail = 1;
             // leftover halves (at most split_round) and the half tiles (at most one per group)
             const unsigned grid = (unsigned)m.split_round + (unsigned)m.max_half * (unsigned)m.n_tiles;
-            grouped_gemm_kernel<128, 2, 2, MODE><<<grid, kThreads, 0, stream>>>(t);
+            grouped_gemm_kernel<128, 2, 2, MODE, ABLK><<<grid, kThreads, 0, stream>>>(t);
             return hipGetLastError();
         }
         case 128: {
             GemmArgs m = a;
             m.split_round = 0;
             m.tail = 0;
-            return launch_cfg<128, 2, 2, MODE>(m, stream);
+            return launch_cfg<128, 2, 2, MODE, ABLK>(m, stream);
         }
         case 64: {
             GemmArgs m = a;
             m.split_round = 0;
             m.tail = 0;
-            return launch_cfg<64, 1, 4, MODE>(m, stream);
+            return launch_cfg<64, 1, 4, MODE, ABLK>(m, stream);
         }
         default: return hipErrorInvalidValue;
     }
@@ -732,13 +763,13 @@ hipError_t launch_mode(int block_m, const GemmArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_linear1(int block_m, const GemmArgs& a, hipStream_t stream) {
-    return launch_mode<1>(block_m, a, stream);
+    return a.a_blocked ? launch_mode<1, true>(block_m, a, stream) : launch_mode<1, false>(block_m, a, stream);
 }
 hipError_t launch_linear2(int block_m, const GemmArgs& a, hipStream_t stream) {
-    return launch_mode<2>(block_m, a, stream);
+    return launch_mode<2, true>(block_m, a, stream);
 }
 hipError_t launch_gemm_plain(int block_m, const GemmArgs& a, hipStream_t stream) {
-    return launch_mode<3>(block_m, a, stream);
+    return launch_mode<3, false>(block_m, a, stream);
 }
 hipError_t launch_gemm_splitk(int block_m, const GemmArgs& a, hipStream_t stream) {
     if (a.max_tiles == 0 || a.n_tiles == 0) return hipSuccess;
@@ -747,9 +778,9 @@ hipError_t launch_gemm_splitk(int block_m, const GemmArgs& a, hipStream_t stream
     m.tail = 0;
     const unsigned grid = (unsigned)m.max_tiles * (unsigned)m.n_tiles * (unsigned)m.splits;
     if (block_m == 128)
-        grouped_gemm_kernel<128, 2, 2, 4><<<grid, kThreads, 0, stream>>>(m);
+        grouped_gemm_kernel<128, 2, 2, 4, false><<<grid, kThreads, 0, stream>>>(m);
     else if (block_m == 64)
-        grouped_gemm_kernel<64, 1, 4, 4><<<grid, kThreads, 0, stream>>>(m);
+        grouped_gemm_kernel<64, 1, 4, 4, false><<<grid, kThreads, 0, stream>>>(m);
     else
         return hipErrorInvalidValue;
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;

@@ -86,7 +86,7 @@ WsLayout ws_layout(const moe_shape_t& s) {
     w.pub.stage = take(slots * H * sizeof(uint16_t));
     const bool copy = s.num_topk <= kDispatchCopyMaxTopk;
     w.pub.xg = take(copy ? ppad * H : 0);
-    w.pub.xg_sf = take(copy ? ppad * 4 * ((H + 511) / 512) : 0);
+    w.pub.xg_sf = take(ppad * 4 * ((H + 511) / 512));
     w.pub.total = off;
     w.pub.max_tiles = (int32_t)max_tiles;
     w.max_pad_rows = (int)ppad;
@@ -178,15 +178,17 @@ static int forward_impl(uint16_t* y_bf16, const uint8_t* x_fp8, const uint8_t* x
     int32_t* tile_e = i32(W.pub.tile_expert);
     int32_t* tile_r = i32(W.pub.tile_row0);
 
+    // The gather copies the scale rows of the dispatched tokens into the blocked scale copy
+    // xg_sf for every top-k, and the x rows themselves only for top-k <= 2.
+    const int xsfs = 4 * ((H + 511) / 512);
+    const bool dispatch_copy = k <= kDispatchCopyMaxTopk;
     if (mark(0) != hipSuccess) return MOE_ERR_HIP;
     if (launch_route(topk_idx, T * k, E, BM, i32(W.blk), meta, i32(W.pub.counts),
                      i32(W.pub.offsets), perm, i32(W.pub.inv), tile_e, tile_r, W.pub.max_tiles,
                      stream) != hipSuccess)
         return MOE_ERR_HIP;
-    const int xsfs = 4 * ((H + 511) / 512);
-    const bool dispatch_copy = k <= kDispatchCopyMaxTopk;
-    if (dispatch_copy && launch_gather(x_fp8, x_sf, perm, meta, k, H, xsfs, BM, W.max_pad_rows,
-                                       ws + W.pub.xg, ws + W.pub.xg_sf, stream) != hipSuccess)
+    if (launch_gather(x_fp8, x_sf, perm, meta, k, H, xsfs, BM, W.max_pad_rows,
+                      dispatch_copy ? ws + W.pub.xg : nullptr, ws + W.pub.xg_sf, stream) != hipSuccess)
         return MOE_ERR_HIP;
     if (mark(1) != hipSuccess) return MOE_ERR_HIP;
 
@@ -201,7 +203,7 @@ static int forward_impl(uint16_t* y_bf16, const uint8_t* x_fp8, const uint8_t* x
     a1.max_half = E;      // the routing may list one half tile per expert
     a1.dense_rows = 0;
     a1.a = dispatch_copy ? ws + W.pub.xg : x_fp8;
-    a1.a_sf = dispatch_copy ? ws + W.pub.xg_sf : x_sf;
+    a1.a_sf = ws + W.pub.xg_sf;
     a1.a_blocked = dispatch_copy ? 1 : 0;
     a1.a_stride = H;
     a1.a_sf_stride = xsfs;

@@ -31,6 +31,18 @@ constexpr int kBScaleBlockBytes = 16 * 64 * 4;
 constexpr int kHalfTileRows = 128;
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Word index of the blocked UE8M0 scales of the dispatched activations (xg_sf) and of h
+// (h_sf): padded rows in blocks of hblk rows (a multiple of 64), `words` 32-bit words per
+// row (word w holds the bytes of 128-column blocks 4w .. 4w+3). Block b stores its rows'
+// word 0, then word 1, ...; within each 64-row group, row 16f + i (f < 4, i < 16) sits at
+// position 4i + f, so that a GEMM lane reads the words of rows i, 16+i, 32+i, 48+i (its
+// four 16-row fragments) as one 16-byte load.
+__host__ __device__ inline uint32_t blocked_scale_word(uint32_t p, uint32_t w, uint32_t words, uint32_t hblk) {
+    const uint32_t r = p % hblk;
+    const uint32_t pos = (r & ~63u) | ((r & 15u) << 2) | ((r >> 4) & 3u);
+    return ((p / hblk) * words + w) * hblk + pos;
+}
 inline int cdiv(int a, int b) { return (a + b - 1) / b; }
 
 // Offsets of the four regions of the packed weight buffer.
@@ -134,8 +146,9 @@ hipError_t launch_gemm_layout(int G, int max_m, const int32_t* masked_m, int blo
 hipError_t launch_cast_fp8(const uint16_t* x, int rows, int cols, uint8_t* q, uint8_t* sf,
                            hipStream_t stream);
 
-// Dispatch copy (route.hip): the x row and scales of each padded row's token into the
-// blocked A layout of Linear1 (zero on padding rows)
+// Dispatch copy (route.hip): the x row (when xg is not null) and the scale row of each
+// padded row's token into the blocked A layout of Linear1 and the blocked scale layout
+// (zero on padding rows)
 hipError_t launch_gather(const uint8_t* x, const uint8_t* x_sf, const int32_t* perm,
                          const int32_t* meta, int k, int H, int sfs, int hblk, int max_rows,
                          uint8_t* xg, uint8_t* xg_sf, hipStream_t stream);

@@ -310,7 +310,10 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(
 // Dispatch copy: thread d writes bytes [16d, 16d+16) of the blocked buffer
 // [P_pad/hblk][H/128][hblk][128] (consecutive threads, consecutive bytes): padded row
 // p = blk*hblk + r, columns kb*128 + 16*c8 .. +15, from the x row of token perm[p]/k (zero
-// on padding rows). The first rows*sfs/4 threads also copy one 32-bit scale word each.
+// on padding rows). With xg null only the scales are copied. The first rows*sfs/4 threads
+// write word d of the blocked scale copy (consecutive threads, consecutive words): its
+// padded row and word index come from inverting blocked_scale_word, its value from the
+// token's scale row (zero on padding rows).
 __global__ __launch_bounds__(256) void gather_kernel(const uint8_t* __restrict__ x,
                                                      const uint8_t* __restrict__ x_sf,
                                                      const int32_t* __restrict__ perm,
@@ -322,7 +325,7 @@ __global__ __launch_bounds__(256) void gather_kernel(const uint8_t* __restrict__
     if (rows > max_rows) rows = max_rows;
     const size_t d = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
     const int nkb = H / 128;
-    if (d < (size_t)rows * (H / 16)) {
+    if (xg != nullptr && d < (size_t)rows * (H / 16)) {
         const int c8 = (int)(d & 7);
         const size_t q = d >> 3;
         const int r = (int)(q % hblk);
@@ -330,17 +333,21 @@ __global__ __launch_bounds__(256) void gather_kernel(const uint8_t* __restrict__
         const int kb = (int)(q2 % nkb);
         const int blk = (int)(q2 / nkb);
         const int p = blk * hblk + r;
-        const int slot = perm[p];
+        const int slot = p < rows ? perm[p] : -1;
         uint4 v = make_uint4(0u, 0u, 0u, 0u);
         if (slot >= 0) v = *reinterpret_cast<const uint4*>(x + (size_t)(slot / k) * H + kb * 128 + c8 * 16);
         *reinterpret_cast<uint4*>(xg + d * 16) = v;
     }
     const int words = sfs / 4;
     if (d < (size_t)rows * words) {
-        const int p = (int)(d / words), w = (int)(d % words);
-        const int slot = perm[p];
+        const uint32_t per_blk = (uint32_t)words * (uint32_t)hblk;
+        const uint32_t blk = (uint32_t)(d / per_blk), rem = (uint32_t)(d % per_blk);
+        const uint32_t w = rem / (uint32_t)hblk, pos = rem % (uint32_t)hblk;
+        const uint32_t r = (pos & ~63u) | ((pos & 3u) << 4) | ((pos >> 2) & 15u);   // 4i + f -> 16f + i
+        const int p = (int)(blk * hblk + r);
+        const int slot = p < rows ? perm[p] : -1;
         const uint32_t v = slot >= 0 ? reinterpret_cast<const uint32_t*>(x_sf + (size_t)(slot / k) * sfs)[w] : 0u;
-        reinterpret_cast<uint32_t*>(xg_sf + (size_t)p * sfs)[w] = v;
+        reinterpret_cast<uint32_t*>(xg_sf)[d] = v;
     }
 }
 
@@ -421,7 +428,8 @@ hipError_t launch_gemm_layout(int G, int max_m, const int32_t* masked_m, int blo
 hipError_t launch_gather(const uint8_t* x, const uint8_t* x_sf, const int32_t* perm,
                          const int32_t* meta, int k, int H, int sfs, int hblk, int max_rows,
                          uint8_t* xg, uint8_t* xg_sf, hipStream_t stream) {
-    const size_t n = (size_t)max_rows * (H / 16);
+    // one thread per 16 bytes of x copy, or per scale word when only the scales are copied
+    const size_t n = (size_t)max_rows * (xg != nullptr ? H / 16 : sfs / 4);
     if (n == 0) return hipSuccess;
     gather_kernel<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(x, x_sf, perm, meta, k, H, sfs, hblk,
                                                                   max_rows, xg, xg_sf);

@@ -139,14 +139,21 @@ typedef struct {
                                [P_pad/block_m][I/128][block_m][128]: padded row p, column c
                                at ((p/block_m)*(I/128) + c/128)*block_m*128 + (p%block_m)*128
                                + c%128 */
-    size_t h_sf;            /* u8 [P_pad, 4*ceil(I/512)] its UE8M0 scales */
-    size_t h_sf_stride;     /* bytes per h_sf row */
+    size_t h_sf;            /* u8 its UE8M0 scales, one byte per (padded row, 128-column
+                               block), in the blocked scale layout: with W = h_sf_stride/4
+                               32-bit words per row (word w = bytes of blocks 4w..4w+3) and
+                               r = p % block_m, word w of row p is word
+                               ((p/block_m)*W + w)*block_m + (r/64)*64 + (r%16)*4 + (r/16)%4
+                               (within 64 rows, row 16f+i at 4i+f) */
+    size_t h_sf_stride;     /* scale bytes per row (4*ceil(I/512)) */
     size_t stage;           /* u16[T*k, H]  weighted bf16 Linear2 rows, by slot */
     size_t xg;              /* u8 the dispatched activations, only when num_topk <= 2 (zero
-                               bytes otherwise: xg == xg_sf == total): the x row of each padded
-                               row's token (zero on padding rows), blocked like h8 with H
-                               columns: [P_pad/block_m][H/128][block_m][128] */
-    size_t xg_sf;           /* u8 [P_pad, 4*ceil(H/512)] their UE8M0 scales (num_topk <= 2) */
+                               bytes otherwise: xg == xg_sf): the x row of each padded row's
+                               token (zero on padding rows), blocked like h8 with H columns:
+                               [P_pad/block_m][H/128][block_m][128] */
+    size_t xg_sf;           /* u8 the scale rows of the dispatched tokens (for every top-k),
+                               4*ceil(H/512) bytes per padded row in the blocked scale layout
+                               of h_sf, zero on padding rows */
     size_t total;           /* bytes used */
 } moe_layout_t;
 

@@ -61,7 +61,8 @@ class Run:
 
     def intermediates(self, rows, T=None):
         """h8 codes [len(rows), I] and h_sf bytes [len(rows), I/128] of the given padded rows
-        (h8 is stored in blocks of block_m rows x 128 columns; h_sf row-major)."""
+        (h8 is stored in blocks of block_m rows x 128 columns; h_sf in the blocked scale
+        layout of moe.h)."""
         L = self.layout(self.last_T if T is None else T)
         I = self.shape.intermediate
         hb = L["block_m"]
@@ -73,11 +74,26 @@ class Run:
         h8 = h8.permute(0, 2, 1, 3).reshape(nblk * hb, I)
         rt = torch.as_tensor(rows, device=self.ws.device)
         h8 = h8[rt].cpu().numpy()
-        hs = self.ws[L["h_sf"]: L["h_sf"] + n * sfs].view(n, sfs)[rt][:, : I // 128].cpu().numpy()
+        words = sfs // 4
+        raw = self.ws[L["h_sf"]: L["h_sf"] + nblk * hb * sfs].cpu().numpy()
+        hs = raw[blocked_scale_bytes(rows, I // 128, words, hb)]
         return h8, hs
 
 
 HALF_TILE_ROWS = 128
+
+
+def blocked_scale_bytes(rows, nblocks, words, hblk):
+    """Byte offsets [len(rows), nblocks] of the scale byte of (padded row, 128-column block)
+    in the blocked scale layout (include/moe.h): rows in blocks of hblk, block b holding
+    word 0 of its rows, then word 1, ...; within each 64-row group, row 16f + i at position
+    4i + f; byte j % 4 of word j // 4."""
+    p = np.asarray(rows, dtype=np.int64)[:, None]
+    j = np.arange(nblocks, dtype=np.int64)[None, :]
+    r = p % hblk
+    pos = (r // 64) * 64 + (r % 16) * 4 + (r // 16) % 4
+    word = ((p // hblk) * words + j // 4) * hblk + pos
+    return word * 4 + j % 4
 
 
 def scheduled_tile_list(ref: dict, block_m: int):

@@ -103,4 +103,6 @@ def test_accumulators_stay_tied_and_in_place(asm):
         moves = [l for l in body if l.startswith(("v_accvgpr_read", "v_accvgpr_write", "v_accvgpr_mov"))]
         assert not moves, moves[:4]
         assert not [l for l in body if l.startswith("scratch_")]
-    assert n_mfma_loops == 11     # Linear1, Linear2, plain GEMM: three row-tile classes; split-K: two
+    # Linear1 (A blocked or through the row list), Linear2, plain GEMM: three row-tile classes
+    # each; split-K: two
+    assert n_mfma_loops == 14
