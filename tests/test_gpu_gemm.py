@@ -177,6 +177,28 @@ def test_grouped_gemms_with_the_most_groups():
     assert np.array_equal(d2, d), "contiguous and masked layouts of the same rows differ"
 
 
+def test_masked_gemm_packed_b_beyond_4gb():
+    """Packed B above 4 GB: byte offsets into it no longer fit 32 bits, so the kernels read B
+    through a descriptor based at each tile instead of one for the whole region (every
+    smaller shape takes the other path). The last groups lie past 4 GB."""
+    G, N, K = 300, 4096, 7168
+    cfg = GemmConfig("g_masked_4g", "masked", M=4, N=N, K=K, G=G, expected_m=2)
+    assert moe.moe_gemm_packed_b_bytes(G, N, K) > 2 ** 32
+    print(f"[gemm] {cfg}", flush=True)
+    inp = make_gemm_inputs(cfg, seed=8, device="cuda")
+    run = GemmRun(inp)
+    d = run.run().reshape(G, cfg.M, N)
+    cnt = np.clip(_host(inp.masked_m), 0, cfg.M)
+    a, a_sf = _host(inp.a), _host(inp.a_sf)
+    for g in (0, G // 2, G - 8, G - 1):
+        c = int(cnt[g])
+        assert (d[g, c:] == POISON).all()
+        ref = oracle.fp8_fp4_gemm(a[g, :c], a_sf[g, :c], _host(inp.b[g]), _host(inp.b_sf[g]), K)
+        _check_rows(d[g], np.arange(c), np.arange(c), ref)
+    del run, inp
+    torch.cuda.empty_cache()
+
+
 def test_masked_gemm_graph_replays_follow_device_counts():
     """Captured once, replayed with counts changed on the device between replays: each replay
     computes the rows the counts name at that time (the host never reads them)."""
