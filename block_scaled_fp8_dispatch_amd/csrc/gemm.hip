@@ -206,13 +206,17 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
     // mt*hblk .. mt*hblk+hblk-1 of group 0 (hblk = the launch's tile rows, which the tail
     // launch runs as two halves), and rows at or past dense_rows are padding
     const bool dense = MODE >= 3 && args.dense_rows > 0;
-    int num_mt = dense ? (args.dense_rows + args.hblk - 1) / args.hblk : args.meta[0];
+    // Tile metadata read from memory is uniform across the workgroup; readfirstlane says so,
+    // so that every address and buffer descriptor derived from it stays in scalar registers
+    // (where the compiler cannot prove it, a descriptor in vector registers turns each tile
+    // load into a loop over lanes).
+    int num_mt = dense ? (args.dense_rows + args.hblk - 1) / args.hblk : __builtin_amdgcn_readfirstlane(args.meta[0]);
     if (num_mt > args.max_tiles) num_mt = args.max_tiles;
     // Half tiles go to the second launch only where K is long: there a 128-row tile takes
     // about 0.6 of a 256-row tile's time; with short K the fixed costs of a tile dominate and
     // they stay in the first launch as ordinary 256-row tiles (both launches decide alike).
     const bool defer_half = !dense && args.K >= kHalfTileMinK;
-    const int n_full = defer_half ? min(args.meta[3], num_mt) : num_mt;
+    const int n_full = defer_half ? min(__builtin_amdgcn_readfirstlane(args.meta[3]), num_mt) : num_mt;
     const int NT = args.n_tiles;
     const int S = MODE == 4 ? args.splits : 1;   // split-K: S workgroups per output tile
     const int total = n_full * NT * S;
@@ -251,8 +255,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
         mt = mt0 + vin % gm;
         nt = vin / gm;
     }
-    const int expert = dense ? 0 : args.tile_expert[mt];
-    const int row0 = (dense ? mt * args.hblk : args.tile_row0[mt]) + half * BM;
+    const int expert = dense ? 0 : __builtin_amdgcn_readfirstlane(args.tile_expert[mt]);
+    const int row0 = (dense ? mt * args.hblk : __builtin_amdgcn_readfirstlane(args.tile_row0[mt])) + half * BM;
     // K steps of this workgroup: all of them, or (split-K) the split's range, which starts at
     // a multiple of 4 so that scale words and byte selects line up
     const int k_begin = MODE == 4 ? split * args.ks_split : 0;
@@ -318,22 +322,15 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
     };
     const __amdgpu_buffer_rsrc_t rs_a = __builtin_amdgcn_make_buffer_rsrc((void*)args.a, 0, kAllRecords, kRsrcWord3);
     const __amdgpu_buffer_rsrc_t rs_asf = __builtin_amdgcn_make_buffer_rsrc((void*)args.a_sf, 0, kAllRecords, kRsrcWord3);
-    // B and its scales: where every offset into the packed region fits 32 bits (all forward
-    // shapes), one descriptor at the region's start for every tile, with the tile's byte
-    // offset in the per-lane offset; otherwise a descriptor based at the tile. A descriptor
-    // base that differs between tiles costs about 350 cycles per K step in the tile loads
-    // (measured at 256x256 tiles: 2763 -> 2415 cycles per step), the same data through one
-    // shared descriptor does not.
-    const size_t b_tile = (size_t)expert * args.b_expert + (size_t)nt * args.b_ntile + (size_t)k_begin * kBTileBytes;
-    const size_t bs_tile = (size_t)expert * args.bs_expert + (size_t)nt * args.bs_ntile +
-                           (size_t)(k_begin / 4) * (kBScaleBlockBytes / 4);   // 32-bit words
-    const bool b_flat = args.b_flat != 0;
     const __amdgpu_buffer_rsrc_t rs_b = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(b_flat ? args.b : args.b + b_tile), 0, kAllRecords, kRsrcWord3);
+        (void*)(args.b + (size_t)expert * args.b_expert + (size_t)nt * args.b_ntile + (size_t)k_begin * kBTileBytes),
+        0, kAllRecords, kRsrcWord3);
     const __amdgpu_buffer_rsrc_t rs_bsf = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(b_flat ? args.b_sf : args.b_sf + bs_tile), 0, kAllRecords, kRsrcWord3);
-    const uint32_t b_voff = (uint32_t)(wave * B_DMA * 1024 + lane * 16) + (b_flat ? (uint32_t)b_tile : 0u);
-    const uint32_t bs_voff = (uint32_t)(lane * 4) + (b_flat ? (uint32_t)(4 * bs_tile) : 0u);
+        (void*)(args.b_sf + (size_t)expert * args.bs_expert + (size_t)nt * args.bs_ntile +
+                (size_t)(k_begin / 4) * (kBScaleBlockBytes / 4)),
+        0, kAllRecords, kRsrcWord3);
+    const uint32_t b_voff = (uint32_t)(wave * B_DMA * 1024 + lane * 16);
+    const uint32_t bs_voff = (uint32_t)(lane * 4);
 
     // one direct-to-LDS load (j < A_DMA: A rows, else B fragments) of K step ks into ring
     // slot `slot` (ks is clamped by the caller)
@@ -558,15 +555,25 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
             const uint32_t hsf_u = 4u * (((uint32_t)(row0 / args.hblk) * hsf_words + ((uint32_t)nt >> 2)) *
                                          (uint32_t)args.hblk + hsf_base) + (uint32_t)(nt & 3);
             const uint32_t hsf_lane = 64u * (uint32_t)g;
+            // the block maxima of all the lane's rows first (one batch of LDS reads), then the
+            // scale bytes, then codes and stores; the scale bytes go out in one masked pass
+            uint32_t mbv[FM][4];
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int rt = wm * WM + fm * 16 + 4 * g + r;
+                    mbv[fm][r] = red[rt];
+#pragma unroll
+                    for (int w = 1; w < WAVES_N; ++w) mbv[fm][r] = max(mbv[fm][r], red[w * BM + rt]);
+                }
+            int bytes[FM][4];
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int rt = wm * WM + fm * 16 + 4 * g + r;
-                    uint32_t mb = red[rt];
-#pragma unroll
-                    for (int w = 1; w < WAVES_N; ++w) mb = max(mb, red[w * BM + rt]);
-                    const int byte = requant_scale_byte(__uint_as_float(mb));
+                    const int byte = requant_scale_byte(__uint_as_float(mbv[fm][r]));
+                    bytes[fm][r] = byte;
                     const float mul = __uint_as_float((uint32_t)(254 - byte) << 23);  // 2^-(byte-127)
                     int pk = __builtin_amdgcn_cvt_pk_fp8_f32(acc[fm][0][r] * mul, acc[fm][1][r] * mul, 0, false);
                     if constexpr (FQ == 4) {
@@ -577,10 +584,15 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
                         __builtin_amdgcn_raw_buffer_store_b16((uint16_t)pk, rs_h8, h_lane,
                                                               h_blk + (uint32_t)(fm * 16 + r) * 128u, 0);
                     }
-                    if (wn == 0 && l == 0)   // the scale byte of (row, block nt)
-                        __builtin_amdgcn_raw_buffer_store_b8(
-                            (uint8_t)byte, rs_hsf, hsf_lane + 4u * (64u * (fm / 4) + 4u * r + fm % 4), hsf_u, 0);
                 }
+            }
+            if (wn == 0 && l == 0) {   // the scale bytes of (row, block nt)
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        __builtin_amdgcn_raw_buffer_store_b8(
+                            (uint8_t)bytes[fm][r], rs_hsf, hsf_lane + 4u * (64u * (fm / 4) + 4u * r + fm % 4), hsf_u, 0);
             }
         } else if constexpr (MODE == 4) {
             // Split-K: the FP32 sums of this K range, row-major [BM][256] per (tile, split),

@@ -98,7 +98,6 @@ GemmArgs plain_args(const uint8_t* a, const uint8_t* a_sf, int N, int K, const v
     g.b_ntile = L.d_ntile;
     g.bs_expert = L.s_group / 4;
     g.bs_ntile = L.s_ntile / 4;
-    g.b_flat = L.total <= 0xFFFFFFFFull;
     g.hblk = BM;
     g.stage = d;
     g.topk_weights = nullptr;

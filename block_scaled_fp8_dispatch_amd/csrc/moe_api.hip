@@ -221,7 +221,6 @@ static int forward_impl(uint16_t* y_bf16, const uint8_t* x_fp8, const uint8_t* x
     a1.b_ntile = L.w1d_ntile;
     a1.bs_expert = L.w1s_expert / 4;
     a1.bs_ntile = L.w1s_ntile / 4;
-    a1.b_flat = (size_t)E * L.w1d_expert <= 0xFFFFFFFFull && (size_t)E * L.w1s_expert <= 0xFFFFFFFFull;
     a1.h8 = ws + W.pub.h8;
     a1.h_sf = ws + W.pub.h_sf;
     a1.h_stride = I;
@@ -244,7 +243,6 @@ static int forward_impl(uint16_t* y_bf16, const uint8_t* x_fp8, const uint8_t* x
     a2.b_ntile = L.w2d_ntile;
     a2.bs_expert = L.w2s_expert / 4;
     a2.bs_ntile = L.w2s_ntile / 4;
-    a2.b_flat = (size_t)E * L.w2d_expert <= 0xFFFFFFFFull && (size_t)E * L.w2s_expert <= 0xFFFFFFFFull;
     a2.stage = reinterpret_cast<uint16_t*>(ws + W.pub.stage);
     a2.topk_weights = topk_weights;
     a2.out_cols = H;

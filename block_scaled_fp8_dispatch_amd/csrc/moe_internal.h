@@ -97,7 +97,6 @@ struct GemmArgs {
     const uint32_t* b_sf;
     size_t b_expert, b_ntile;        // bytes
     size_t bs_expert, bs_ntile;      // 32-bit words
-    int b_flat;                      // 1: every byte offset into b and b_sf fits 32 bits
     // h8 is stored in blocks of hblk rows x 128 columns, [P_pad/hblk][I/128][hblk][128]: the
     // block a Linear1 tile writes is the A block one Linear2 K step reads, contiguous
     int hblk;

@@ -178,9 +178,8 @@ def test_grouped_gemms_with_the_most_groups():
 
 
 def test_masked_gemm_packed_b_beyond_4gb():
-    """Packed B above 4 GB: byte offsets into it no longer fit 32 bits, so the kernels read B
-    through a descriptor based at each tile instead of one for the whole region (every
-    smaller shape takes the other path). The last groups lie past 4 GB."""
+    """Packed B above 4 GB: the last groups lie past 4 GB from the start of the packed buffer
+    (the kernels' 32-bit buffer offsets are relative to each tile's own B)."""
     G, N, K = 300, 4096, 7168
     cfg = GemmConfig("g_masked_4g", "masked", M=4, N=N, K=K, G=G, expected_m=2)
     assert moe.moe_gemm_packed_b_bytes(G, N, K) > 2 ** 32
