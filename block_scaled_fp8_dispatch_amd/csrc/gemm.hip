@@ -35,7 +35,8 @@
 // steps are branch-free and carry scheduling-group hints, so the compiler places one load
 // between consecutive MFMAs instead of issuing the loads as a burst. Scales are read
 // straight from global memory: one 32-bit word per lane covers four K steps, and the
-// instruction's byte select picks the step.
+// instruction's byte select picks the step. B words come one per fragment; the forward's A
+// words come four fragments at a time, one 16-byte load from the blocked scale layout.
 //
 // Operand layout of the 16x16x128 instruction with A = FP8, B = FP4 (measured on gfx950):
 //   A lane 16g+i : row i, bytes 0..15 = K[16g, 16g+16), bytes 16..31 = K[64+16g, 64+16g+16)
