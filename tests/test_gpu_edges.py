@@ -142,6 +142,37 @@ def _run_once(inp):
     return run, y
 
 
+def test_half_tiles_of_several_sizes():
+    """With 256-row tiles and K >= 4096, each expert's last tile of at most 128 rows (a half
+    tile) runs in the second launch as a 128-row tile. Experts whose last tiles hold 40, 64,
+    65 and 128 rows; the sampled tokens include the first and last rows of every half tile."""
+    tails = [40, 64, 65, 128]
+    counts = [512 + t for t in tails]
+    T, E, H, I = sum(counts), 4, 4096, 4096
+    cfg = MoEConfig("edge", T=T, E=E, k=1, H=H, I=I)
+    print(f"[edge] half tiles of {tails} rows {cfg}", flush=True)
+    inp = make_inputs(cfg, seed=21, device="cuda")
+    idx = np.concatenate([np.full(c, e, np.int32) for e, c in enumerate(counts)])
+    idx = np.random.default_rng(3).permutation(idx).reshape(T, 1)
+    inp = dataclasses.replace(inp, topk_idx=torch.from_numpy(idx).cuda())
+    run = Run(inp)
+    y = run.forward(poison=True)
+    got = run.routing()
+    assert got["block_m"] == 256
+    r = check_routing(got, idx, E)
+    assert list(r["counts"]) == counts
+    toks = set()
+    for e in range(E):
+        rows = np.nonzero(idx[:, 0] == e)[0]
+        toks.update(int(t) for t in rows[-3:])              # the expert's last tile
+        toks.update(int(t) for t in rows[511:513])         # last row of a full tile, first of the half tile
+    toks.update(int(t) for t in np.random.default_rng(4).choice(T, 6, replace=False))
+    toks = sorted(toks)
+    ref = oracle.forward_inputs(_host(inp), tokens=toks, keep_bounds=True)
+    check_intermediates(run, ref, got["inv"])
+    check_y(y, ref, tokens=toks)
+
+
 def test_deterministic():
     print(f"[inv] determinism {CFG_INV}", flush=True)
     inp = make_inputs(CFG_INV, seed=21, device="cuda")
