@@ -15,7 +15,28 @@ __device__ inline uint16_t f32_to_bf16_rne(float v) {
     return (uint16_t)(b >> 16);
 }
 
-// One thread per 8 output columns (16 bytes) of one token.
+__device__ inline void add_bf16x8(float (&acc)[8], const uint4 v) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        acc[2 * q] += __uint_as_float(w[q] << 16);
+        acc[2 * q + 1] += __uint_as_float(w[q] & 0xffff0000u);
+    }
+}
+
+__device__ inline uint4 pack_bf16x8(const float (&acc)[8]) {
+    uint4 o;
+    o.x = f32_to_bf16_rne(acc[0]) | ((uint32_t)f32_to_bf16_rne(acc[1]) << 16);
+    o.y = f32_to_bf16_rne(acc[2]) | ((uint32_t)f32_to_bf16_rne(acc[3]) << 16);
+    o.z = f32_to_bf16_rne(acc[4]) | ((uint32_t)f32_to_bf16_rne(acc[5]) << 16);
+    o.w = f32_to_bf16_rne(acc[6]) | ((uint32_t)f32_to_bf16_rne(acc[7]) << 16);
+    return o;
+}
+
+// One thread per 8 output columns (16 bytes) of one token. KMAX > 0: k <= KMAX, and the
+// loads of all the token's slots are issued before the sums (which still run in slot
+// order); KMAX = 0: any k, one slot at a time.
+template <int KMAX>
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ stage,
                                                       const int32_t* __restrict__ topk_idx,
                                                       int T, int k, int E, int H,
@@ -25,24 +46,26 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
     if (idx >= (size_t)T * per_row) return;
     const int t = (int)(idx / per_row);
     const int c8 = (int)(idx % per_row);
+    const uint16_t* src = stage + (size_t)t * k * H + c8 * 8;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-        const int e = topk_idx[(size_t)t * k + j];
-        if (e < 0 || e >= E) continue;
-        const uint4 v = *reinterpret_cast<const uint4*>(stage + ((size_t)t * k + j) * H + c8 * 8);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    if constexpr (KMAX > 0) {
+        uint4 v[KMAX];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            acc[2 * q] += __uint_as_float(w[q] << 16);
-            acc[2 * q + 1] += __uint_as_float(w[q] & 0xffff0000u);
+        for (int j = 0; j < KMAX; ++j) {
+            const int e = j < k ? topk_idx[(size_t)t * k + j] : -1;
+            v[j] = (e >= 0 && e < E) ? *reinterpret_cast<const uint4*>(src + (size_t)j * H)
+                                     : make_uint4(0u, 0u, 0u, 0u);   // +0 adds nothing
+        }
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) add_bf16x8(acc, v[j]);
+    } else {
+        for (int j = 0; j < k; ++j) {
+            const int e = topk_idx[(size_t)t * k + j];
+            if (e < 0 || e >= E) continue;
+            add_bf16x8(acc, *reinterpret_cast<const uint4*>(src + (size_t)j * H));
         }
     }
-    uint4 o;
-    o.x = f32_to_bf16_rne(acc[0]) | ((uint32_t)f32_to_bf16_rne(acc[1]) << 16);
-    o.y = f32_to_bf16_rne(acc[2]) | ((uint32_t)f32_to_bf16_rne(acc[3]) << 16);
-    o.z = f32_to_bf16_rne(acc[4]) | ((uint32_t)f32_to_bf16_rne(acc[5]) << 16);
-    o.w = f32_to_bf16_rne(acc[6]) | ((uint32_t)f32_to_bf16_rne(acc[7]) << 16);
-    *reinterpret_cast<uint4*>(y + (size_t)t * H + c8 * 8) = o;
+    *reinterpret_cast<uint4*>(y + (size_t)t * H + c8 * 8) = pack_bf16x8(acc);
 }
 
 }  // namespace
@@ -51,7 +74,15 @@ hipError_t launch_combine(const uint16_t* stage, const int32_t* topk_idx, int T,
                           int H, uint16_t* y, hipStream_t stream) {
     const size_t n = (size_t)T * (H / 8);
     if (n == 0) return hipSuccess;
-    combine_kernel<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(stage, topk_idx, T, k, E, H, y);
+    const unsigned grid = (unsigned)((n + 255) / 256);
+    if (k <= 2)
+        combine_kernel<2><<<grid, 256, 0, stream>>>(stage, topk_idx, T, k, E, H, y);
+    else if (k <= 4)
+        combine_kernel<4><<<grid, 256, 0, stream>>>(stage, topk_idx, T, k, E, H, y);
+    else if (k <= 8)
+        combine_kernel<8><<<grid, 256, 0, stream>>>(stage, topk_idx, T, k, E, H, y);
+    else
+        combine_kernel<0><<<grid, 256, 0, stream>>>(stage, topk_idx, T, k, E, H, y);
     return hipGetLastError();
 }
 
