@@ -33,6 +33,22 @@ __device__ inline uint4 pack_bf16x8(const float (&acc)[8]) {
     return o;
 }
 
+// The stage is read once and y is not read again here: both go through non-temporal
+// accesses, which keep them from displacing cached data (c4, a 3.76 GB stage: 826 -> 661 us).
+__device__ inline uint4 load_nt(const uint16_t* p) {
+    const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
+    return make_uint4(__builtin_nontemporal_load(q), __builtin_nontemporal_load(q + 1),
+                      __builtin_nontemporal_load(q + 2), __builtin_nontemporal_load(q + 3));
+}
+
+__device__ inline void store_nt(uint16_t* p, const uint4 v) {
+    uint32_t* q = reinterpret_cast<uint32_t*>(p);
+    __builtin_nontemporal_store(v.x, q);
+    __builtin_nontemporal_store(v.y, q + 1);
+    __builtin_nontemporal_store(v.z, q + 2);
+    __builtin_nontemporal_store(v.w, q + 3);
+}
+
 // One thread per 8 output columns (16 bytes) of one token. KMAX > 0: k <= KMAX, and the
 // loads of all the token's slots are issued before the sums (which still run in slot
 // order); KMAX = 0: any k, one slot at a time.
@@ -53,8 +69,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
 #pragma unroll
         for (int j = 0; j < KMAX; ++j) {
             const int e = j < k ? topk_idx[(size_t)t * k + j] : -1;
-            v[j] = (e >= 0 && e < E) ? *reinterpret_cast<const uint4*>(src + (size_t)j * H)
-                                     : make_uint4(0u, 0u, 0u, 0u);   // +0 adds nothing
+            v[j] = (e >= 0 && e < E) ? load_nt(src + (size_t)j * H) : make_uint4(0u, 0u, 0u, 0u);   // +0 adds nothing
         }
 #pragma unroll
         for (int j = 0; j < KMAX; ++j) add_bf16x8(acc, v[j]);
@@ -62,10 +77,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
         for (int j = 0; j < k; ++j) {
             const int e = topk_idx[(size_t)t * k + j];
             if (e < 0 || e >= E) continue;
-            add_bf16x8(acc, *reinterpret_cast<const uint4*>(src + (size_t)j * H));
+            add_bf16x8(acc, load_nt(src + (size_t)j * H));
         }
     }
-    *reinterpret_cast<uint4*>(y + (size_t)t * H + c8 * 8) = pack_bf16x8(acc);
+    store_nt(y + (size_t)t * H + c8 * 8, pack_bf16x8(acc));
 }
 
 }  // namespace
