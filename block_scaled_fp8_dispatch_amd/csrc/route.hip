@@ -4,10 +4,11 @@
 // The explainer (chenxutan.com/d/1930 section 3.1, step 1) describes dispatch as moving
 // each token to its experts' regions; the contiguous-layout grouped GEMM
 // (juejin.cn/post/7631516744872673307, "MoE模型专属优化") keeps every expert's rows
-// together with each group block-aligned. After the routing, when each token has at most
-// two slots, a copy moves each padded row's activation row and scales into expert order,
-// in the blocked layout the GEMM reads (one contiguous 1 KB piece per load); with more
-// slots per token the GEMM reads x through the row list instead.
+// together with each group block-aligned. After the routing, a copy moves each padded
+// row's scale row into expert order, in the blocked scale layout the GEMM reads, and,
+// when each token has at most two slots, its activation row too, in the blocked layout
+// the GEMM reads (one contiguous 1 KB piece per load); with more slots per token the GEMM
+// reads x rows through the row list instead.
 //
 // The same kernels group the rows of the standalone contiguous-layout GEMM (a top-1
 // routing of rows to groups), and a small layout kernel builds the row and tile lists of
