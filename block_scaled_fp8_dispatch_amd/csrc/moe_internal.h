@@ -71,11 +71,12 @@ hipError_t launch_pack(const moe_shape_t& s, const PackedLayout& L,
 struct GemmArgs {
     // A operand: rows of FP8 codes with per-1x128 UE8M0 scales
     const uint8_t* a;          // A rows: blocked (h8, or the dispatched x) or x itself
-    int a_blocked;             // 1: A blocked like h8, scale rows = padded rows;
-                               // 0 (Linear1 only): rows of x gathered through perm
-    const uint8_t* a_sf;
+    int a_blocked;             // 1: A blocked like h8; 0 (Linear1 only): rows of x
+                               // gathered through perm
+    const uint8_t* a_sf;       // Linear1/2: the blocked scale copy (xg_sf, h_sf), whatever
+                               // a_blocked; plain GEMM: scale rows named by perm
     int a_stride;              // bytes per A row (= K)
-    int a_sf_stride;           // bytes per A scale row
+    int a_sf_stride;           // scale bytes per A row (4*ceil(K/512))
     int K;                     // reduction length (multiple of 128)
     int topk;                  // a_blocked == 0: slot -> token = slot / topk
     const int32_t* perm;       // per padded row: slot (MoE) or A/D row (plain GEMM); -1 padding
