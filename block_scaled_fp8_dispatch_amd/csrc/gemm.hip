@@ -426,9 +426,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
     // each 4-step block the scale words of the next block into the other scale set (needed
     // only after the next barrier, which waits for them), then the A loads of step ks+2
     // into the slot of step ks-1. Steps past the last are clamped to it: a harmless reload
-    // into a free slot. Splitting the loads over both halves keeps the texture-address
-    // queue short; vector-memory counts retire in issue order, so a B load issued before
-    // the A loads of a step waits with them.
+    // into a free slot. Splitting the loads over both halves measured faster than issuing
+    // them all in the second half; vector-memory counts retire in issue order, so a B load
+    // issued before the A loads of a step waits with them.
     // The last A fragment's MFMAs reload each B fragment register with the next step's
     // fragment right after its last use, and the next step's first A fragment is read with
     // them: no double buffers.
