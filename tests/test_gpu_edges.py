@@ -173,6 +173,36 @@ def test_half_tiles_of_several_sizes():
     check_y(y, ref, tokens=toks)
 
 
+@pytest.mark.parametrize("k,BMexp", [(2, 256), (8, 128)])
+def test_dispatch_scale_copy(k, BMexp):
+    """The gather's copy of each padded row's token scale row (xg_sf), read back from the
+    workspace in the blocked scale layout (decoded by the test's own statement of it): equal
+    to the token's x_sf row on every routed row and zero on padding rows, for a top-k with
+    the dispatch copy of x (2) and one without (8)."""
+    E = 8
+    T = 2048 if k == 2 else 160
+    cfg = MoEConfig("edge", T=T, E=E, k=k, H=1280, I=256)
+    print(f"[edge] dispatch scale copy {cfg}", flush=True)
+    inp = make_inputs(cfg, seed=23, device="cuda")
+    run = Run(inp)
+    run.forward(poison=True)
+    got = run.routing()
+    hb = got["block_m"]
+    assert hb == BMexp
+    L = run.layout()
+    words = (cfg.H + 511) // 512
+    rows = np.arange(int(got["meta"][0]) * hb)
+    raw = run.ws[L["xg_sf"]: L["xg_sf"] + len(rows) * 4 * words].cpu().numpy()
+    from gpu_helpers import blocked_scale_bytes
+    nblocks = cfg.H // 128
+    copied = raw[blocked_scale_bytes(rows, nblocks, words, hb)]          # [rows, H/128]
+    perm = got["perm"][: len(rows)]
+    x_sf = inp.x_sf.cpu().numpy()[:, :nblocks]
+    valid = perm >= 0
+    assert np.array_equal(copied[valid], x_sf[perm[valid] // k])
+    assert not copied[~valid].any()
+
+
 def test_deterministic():
     print(f"[inv] determinism {CFG_INV}", flush=True)
     inp = make_inputs(CFG_INV, seed=21, device="cuda")
