@@ -45,9 +45,10 @@
 //   C lane l     : C[4*(l/16) + r][l%16], r = 0..3
 //
 // Launch mapping. Workgroups go round-robin to the 8 XCDs (id mod 8). Each XCD owns a
-// contiguous range of tile ids and its workgroups take consecutive ids in each round;
-// tile ids walk groups of 4 row tiles across all column tiles, so the tiles resident on
-// one XCD at any time share A rows and B columns in its L2.
+// range of tile ids and its workgroups take consecutive ids in each round; tile ids walk
+// groups of 4 row tiles across all column tiles, so the tiles resident on one XCD at any
+// time share A rows and B columns in its L2. Where the groups divide evenly, XCD x takes
+// groups x, x+8, ..., so that neighbouring XCDs share B tiles through the last-level cache.
 #include "moe_internal.h"
 
 namespace moe {
@@ -233,6 +234,18 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
         const int per = main_total >> 3, rem = main_total & 7;
         if (li >= per + (xcd < rem ? 1 : 0)) return;
         v = xcd * per + (xcd < rem ? xcd : rem) + li;
+        // Row groups interleaved over the XCDs (XCD x: groups x, x+8, ...) where that keeps
+        // the split exact (every group full, a multiple of 8 groups): neighbouring groups,
+        // usually rows of one expert, then run on neighbouring XCDs at the same time and
+        // sweep the same column tiles together, so each B tile comes from HBM once and the
+        // second XCD finds it in the last-level cache (with contiguous ranges, one XCD swept
+        // an expert's B once per group, the second time from HBM)
+        const int ng = n_full / kGroupM;
+        if (MODE <= 2 && main_total == total && n_full % kGroupM == 0 && ng % 8 == 0 && ng > 0) {
+            const int gsz = kGroupM * NT;
+            const int j = li / gsz;
+            v = (xcd + 8 * j) * gsz + (li - j * gsz);
+        }
     } else {
         const int u = blockIdx.x;
         const int halves = 2 * (total - main_total);
