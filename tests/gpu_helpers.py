@@ -10,6 +10,9 @@ import oracle
 
 Y_TOL = 2e-2            # max |y_gpu - y_ref| / max |y_ref| per row
 OFF_BY_ONE_MAX = 1e-3   # fraction of requantised FP8 intermediates one code off
+# fewest compared intermediates for which that fraction is checked as a rate (at 1e-3, ten
+# expected differences); smaller samples check every difference against the FP32 bound
+RATE_MIN_ELEMENTS = 10_000
 
 
 class Run:
@@ -151,12 +154,14 @@ _HALF_GAP = _e4m3_half_gap()
 def check_intermediates(run: Run, ref: dict, inv: np.ndarray):
     """Compare GPU h8/h_sf with the oracle's requantised intermediate slot by slot.
 
-    Each element is decoded on both sides. Elements whose values differ count against the
-    0.1% budget. Each must be one step apart on the e4m3 grid at the coarser of the two
-    block scales, or, where the oracle returns h and its FP32 accumulation error bound,
-    the GPU's value must be a round-to-nearest result of some h' within that bound of
-    the exact h (this covers small elements of a block, where the grid is finer than the
-    FP32 error of a dot product that cancels)."""
+    Each element is decoded on both sides. Each element whose values differ must be one
+    step apart on the e4m3 grid at the coarser of the two block scales, or, where the oracle
+    returns h and its FP32 accumulation error bound, the GPU's value must be a
+    round-to-nearest result of some h' within that bound of the exact h (this covers small
+    elements of a block, where the grid is finer than the FP32 error of a dot product that
+    cancels). With at least RATE_MIN_ELEMENTS elements, the differing ones may be at most
+    0.1 % of them; a smaller sample cannot estimate that rate, and there every differing
+    element must be explained by the FP32 bound instead."""
     slots = sorted(ref["h8"].keys())
     if not slots:
         return 0.0
@@ -170,16 +175,26 @@ def check_intermediates(run: Run, ref: dict, inv: np.ndarray):
     dist = oracle.e4m3_code_distance(g8, gs, r8, rs)
     frac = float((dist > 0).mean())
     far = dist > 1
-    if far.any() and ref.get("h"):
+    unexplained = np.zeros_like(far)
+    if ref.get("h"):
         h = np.stack([ref["h"][s] for s in slots])
         hb = np.stack([ref["h_bound"][s] for s in slots])
         scale = np.ldexp(1.0, gs.astype(np.int64) - 127)
         vg = oracle.E4M3_TABLE[g8] * scale
         within = np.abs(vg - h) <= hb + _HALF_GAP[g8] * scale
         far &= ~within
+        unexplained = (dist > 0) & ~within
     assert not far.any(), (f"{int(far.sum())} intermediates further than one code and outside "
                            f"the FP32 accumulation bound (max distance {dist.max()})")
-    assert frac <= OFF_BY_ONE_MAX, f"{frac:.2e} of intermediates differ"
+    if dist.size >= RATE_MIN_ELEMENTS:
+        assert frac <= OFF_BY_ONE_MAX, f"{frac:.2e} of intermediates differ"
+    else:
+        # too few elements to estimate a 0.1 % rate: every differing element must instead be
+        # explained by FP32 accumulation (a round-to-nearest result of some value within the
+        # FP32 accumulation bound of the exact h)
+        assert ref.get("h"), "a small sample needs the oracle's accumulation bounds"
+        assert not unexplained.any(), (f"{int(unexplained.sum())} of {dist.size} intermediates "
+                                       f"differ beyond the FP32 accumulation bound")
     return frac
 
 

@@ -48,3 +48,10 @@ def test_tiny_c0():
 ])
 def test_small_shapes(T, E, k, H, I, seed):
     _full_check(MoEConfig("small", T=T, E=E, k=k, H=H, I=I), seed=seed)
+
+
+@pytest.mark.parametrize("T,E,k", [(T, E, k) for T in (2, 5) for E in (1, 2, 3) for k in range(1, E + 1)])
+def test_tiny_shape_sweep(T, E, k):
+    """Every (E, k) with k <= E <= 3 at two and five tokens (one 64-row tile per expert,
+    most of it padding), full parity."""
+    _full_check(MoEConfig("tiny", T=T, E=E, k=k, H=256, I=256), seed=T * 10 + E * 3 + k)
