@@ -134,7 +134,6 @@ def bench_gemm(args, gcfg):
     import torch
 
     import block_scaled_fp8_dispatch_amd as moe
-    import oracle
     from synth import make_gemm_inputs
     c = gcfg
     inp = make_gemm_inputs(c, seed=args.seed, device="cuda")
@@ -182,6 +181,7 @@ def bench_gemm(args, gcfg):
                       "layout": c.layout, "M": c.M, "N": c.N, "K": c.K, "groups": c.G, "rows_computed": rows},
            "alg_hbm_gbs": round(gbs, 1), "wall_s_timed": round(wall, 3), "roofline": roof, "cpu_baseline": None}
     if not args.no_cpu_baseline:
+        import oracle   # the CPU baseline leg only
         # the oracle on the first rows of group 0 (about 10-30 s of CPU work is the aim)
         n = max(1, min(rows, int(6e10 / (2.0 * c.N * c.K))))
         a = inp.a.reshape(-1, c.K)[:n].cpu().numpy()
@@ -203,7 +203,6 @@ def bench_cast(args, rows=8192, cols=7168):
     import torch
 
     import block_scaled_fp8_dispatch_amd as moe
-    import oracle
     from synth import make_bf16_activations
     x = make_bf16_activations(rows, cols, seed=args.seed, device="cuda")
     q = torch.empty(rows, cols, dtype=torch.uint8, device="cuda")
@@ -222,6 +221,7 @@ def bench_cast(args, rows=8192, cols=7168):
                         "traffic": None},
            "cpu_baseline": None}
     if not args.no_cpu_baseline:
+        import oracle   # the CPU baseline leg only
         n = 1024
         bits = x[:n].view(torch.int16).cpu().numpy().view("uint16")
         t0 = time.perf_counter()
