@@ -62,7 +62,6 @@ constexpr int kGroupM = 4;
 // Shortest K (in elements) for which half tiles run in the second launch
 constexpr int kHalfTileMinK = 32 * kBK;
 constexpr int kThreads = 256;
-constexpr int kStages = 3;   // A ring slots
 // Word 3 of a raw buffer descriptor on gfx950 (32-bit data format, no swizzle); with a zero
 // stride, offsets are plain byte offsets, range-checked against the record count.
 constexpr int kRsrcWord3 = 0x00020000;
@@ -158,7 +157,12 @@ struct Cfg {
     // keep 3 (72 KB, two workgroups per CU)
     static constexpr int KB = BM == 64 ? 3 : 4;
     static constexpr int DB = KB - 1;
-    static constexpr int LDS_BYTES = kStages * A_BYTES + KB * kBTileBytes;
+    // A ring: A loads DA steps ahead into AS = DA + 1 slots. 128-row tiles have the LDS for a
+    // fourth slot (128 KB), which doubles the loads a wave may keep in flight at a barrier
+    // (see the step below); 256-row tiles (160 KB with three) and 64-row tiles keep three.
+    static constexpr int DA = BM == 128 ? 3 : 2;
+    static constexpr int AS = DA + 1;
+    static constexpr int LDS_BYTES = AS * A_BYTES + KB * kBTileBytes;
     static constexpr int A_DMA = A_BYTES / 1024 / 4;   // 1 KB direct-to-LDS loads per wave
     static constexpr int B_DMA = kBTileBytes / 1024 / 4;
     static constexpr int DMA = A_DMA + B_DMA;
@@ -168,6 +172,7 @@ struct Cfg {
     static_assert(MODE != 1 || 4 * WAVES_N * BM <= A_BYTES, "epilogue fits a slot");
     static_assert(MODE == 1 || FN == 8 || FN == 4, "one 16- or 8-byte store per row");
     static_assert(MODE != 4 || BM <= 128, "split-K runs without the tail split");
+    static_assert(DA == 2 || (DA == 3 && DB == 3), "issue orders written for these");
 };
 
 // ABLK: A in the blocked layout (Linear2's h8, Linear1's dispatch copy); otherwise A rows are
@@ -182,10 +187,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
     constexpr int WM = C::WM, WN = C::WN, FM = C::FM, FN = C::FN;
     constexpr int A_BYTES = C::A_BYTES;
     constexpr int A_DMA = C::A_DMA, B_DMA = C::B_DMA, DMA = C::DMA;
-    constexpr int KB = C::KB, DB = C::DB;
+    constexpr int KB = C::KB, DB = C::DB, DA = C::DA, AS = C::AS;
 
     __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS_BYTES];
-    uint8_t* const bring = smem + kStages * A_BYTES;
+    uint8_t* const bring = smem + AS * A_BYTES;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -409,19 +414,32 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
     uint32_t sa[2][FM], sb[2][FN];
 
     // prologue, in the order the steps keep (B, then scales and A): scales of block 0, A
-    // and B of step 0, B of steps 1 .. DB-1, A of step 1; so that at every barrier the
-    // only loads allowed in flight are the B loads issued after the A loads of the next step
+    // and B of step 0, then the loads of the steps before step 0 as the steps would have
+    // issued them. DA = 2: B of steps 1 .. DB-1, A of step 1. DA = 3: B(1), A(1), B(2), A(2).
+    // So that at every barrier the loads allowed in flight are exactly those issued after
+    // the A loads of the next step.
 #pragma unroll
     for (int i = 0; i < NSA + FN; ++i) scale_one(0, i, sa[0], sb[0]);
 #pragma unroll
     for (int j = 0; j < DMA; ++j) dma_one(0, 0, j);
+    if constexpr (DA == 2) {
 #pragma unroll
-    for (int s2 = 1; s2 < DB; ++s2)
+        for (int s2 = 1; s2 < DB; ++s2)
 #pragma unroll
-        for (int j = A_DMA; j < DMA; ++j) dma_one(min(s2, nks - 1), s2, j);
+            for (int j = A_DMA; j < DMA; ++j) dma_one(min(s2, nks - 1), s2, j);
 #pragma unroll
-    for (int j = 0; j < A_DMA; ++j) dma_one(1, 1, j);
-    constexpr int WAIT0 = (DB - 1) * B_DMA + A_DMA;          // everything after B(0)
+        for (int j = 0; j < A_DMA; ++j) dma_one(1, 1, j);
+    } else {
+#pragma unroll
+        for (int s2 = 1; s2 < DA; ++s2) {
+#pragma unroll
+            for (int j = A_DMA; j < DMA; ++j) dma_one(min(s2, nks - 1), s2, j);
+#pragma unroll
+            for (int j = 0; j < A_DMA; ++j) dma_one(min(s2, nks - 1), s2, j);
+        }
+    }
+    // everything after A(0) and B(0)
+    constexpr int WAIT0 = DA == 2 ? (DB - 1) * B_DMA + A_DMA : (DA - 1) * DMA;
     __builtin_amdgcn_s_waitcnt(0x0F70 | (WAIT0 & 15) | (((WAIT0 >> 4) & 3) << 14));
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" :: "n"(WAIT0) : "memory");
 #pragma unroll
@@ -449,20 +467,22 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
         constexpr int OPS = decltype(ops_c)::value;
         constexpr int SET = decltype(set_c)::value;
         constexpr int HALF = FM / 2 * FN;
-        constexpr int NS = OPS == 2 ? NSA + FN : 0;         // scale loads of this step
+        // the scales of the next 4-step block go out with the A loads of its first step
+        constexpr int SOPS = 4 - DA;
+        constexpr int NS = OPS == SOPS ? NSA + FN : 0;      // scale loads of this step
         constexpr int NOPS = NS + A_DMA;                     // second-half loads
         constexpr int PER = (NOPS + HALF - 1) / HALF;
         constexpr int PERB = (B_DMA + HALF - 1) / HALF;      // first-half loads
-        const int slot = ks % kStages;
-        const int slot1 = (ks + 1) % kStages;
-        const int slot2 = (ks + 2) % kStages;
+        const int slot = ks % AS;
+        const int slot1 = (ks + 1) % AS;
+        const int slota = (ks + DA) % AS;
         const int bslot1 = (ks + 1) % KB;
         const int bslotn = (ks + DB) % KB;
-        const int ks2 = min(ks + 2, nks - 1);
+        const int ksa = min(ks + DA, nks - 1);
         const int ksb = min(ks + DB, nks - 1);
         auto issue = [&](int op) __attribute__((always_inline)) {
-            if (op < NS) scale_one(ks2, op, sa[SET ^ 1], sb[SET ^ 1]);
-            else if (op < NOPS) dma_one(ks2, slot2, op - NS);
+            if (op < NS) scale_one(ksa, op, sa[SET ^ 1], sb[SET ^ 1]);
+            else if (op < NOPS) dma_one(ksa, slota, op - NS);
         };
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) {
@@ -485,9 +505,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
                 __builtin_amdgcn_sched_barrier(0x7);
             }
             if (fm == FM / 2 - 1) {
-                // this wave's A and B of step ks+1 have landed (only the B loads of step
-                // ks+DB, issued after A of step ks+1, may still be in flight)
-                constexpr int WN = B_DMA;
+                // this wave's A and B of step ks+1 (and the scales of its block) have landed;
+                // still in flight may be only what was issued after A of step ks+1. DA = 2:
+                // the B loads of step ks+DB. DA = 3: those of steps ks+DB-1 and ks+DB, and
+                // the scales and A loads of step ks-1.
+                constexpr int WN = DA == 2 ? B_DMA
+                                           : 2 * B_DMA + A_DMA + ((OPS + 3) % 4 == SOPS ? NSA + FN : 0);
+                static_assert(WN < 64, "vmcnt range");
                 __builtin_amdgcn_s_waitcnt(0x0F70 | (WN & 15) | (((WN >> 4) & 3) << 14));
                 asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" :: "n"(WN) : "memory");
             }
