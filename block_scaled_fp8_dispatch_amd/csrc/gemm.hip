@@ -30,7 +30,9 @@
 // is one barrier per K step, half way through its MFMAs: it waits for this wave's loads of
 // the next step (only the B loads issued after them may stay in flight). B loads go out in
 // the first half of a step and A loads in the second, so each has between half a step and
-// a step and a half to arrive; after the barrier the next step's B fragments and first A
+// a step and a half to arrive. 128-row tiles load A three steps ahead into a fourth slot,
+// which gives every load a step more; they run the launches that stream weights with
+// little reuse, where loads wait longest. After the barrier the next step's B fragments and first A
 // fragment are read into registers, so MFMAs never wait on LDS at a step boundary. The
 // steps are branch-free and carry scheduling-group hints, so the compiler places one load
 // between consecutive MFMAs instead of issuing the loads as a burst. Scales are read
