@@ -215,12 +215,18 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(
     const int lane = tid & 63, wave = tid >> 6;
     int c = 0;
     if (tid < E) {
-        // per-chunk bases within the expert, in chunk order (exclusive prefix)
-        for (int b = 0; b < nblk; ++b) {
-            int* p = blk_counts + (size_t)b * E + tid;
-            const int v = *p;
-            *p = c;
-            c += v;
+        // per-chunk bases within the expert, in chunk order (exclusive prefix). The counts of
+        // 16 chunks are all loaded before any is replaced, so that their loads overlap (one
+        // load, then its store, per chunk waited out a memory latency per chunk).
+        for (int b0 = 0; b0 < nblk; b0 += 16) {
+            int v[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) v[j] = b0 + j < nblk ? blk_counts[(size_t)(b0 + j) * E + tid] : 0;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                if (b0 + j < nblk) blk_counts[(size_t)(b0 + j) * E + tid] = c;
+                c += v[j];
+            }
         }
     }
     const int pad = (c + block_m - 1) / block_m * block_m;
