@@ -65,6 +65,25 @@ def gemm_source_hash() -> str:
     return code_hash(open(GEMM_SRC, encoding="utf-8").read())
 
 
+def linear1_roofline(T: int, k: int, H: int, I: int, E: int, n_active: int, w1_bytes: float,
+                     linear1_ms: float, traffic):
+    """The roofline object of the Linear1 stage. Algorithmic bytes: W1 and its scales for the
+    experts that receive a row, and per valid slot its x row, h8 row and h_sf bytes;
+    algorithmic FLOP: 4*P*H*I. Below the ridge (peak FLOP/s over HBM bytes/s) the stage is
+    priced against HBM bandwidth, else against the MFMA peak."""
+    P = T * k
+    flop = 4.0 * P * H * I
+    nbytes = w1_bytes * n_active / E + P * (H + I + I // 128)
+    kname = "Linear1 grouped GEMM with SwiGLU/requant epilogue (main + second launch)"
+    if flop / nbytes < PEAK_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
+        gbs = nbytes / (linear1_ms * 1e-3) / 1e9
+        return {"bound": "hbm", "kernel": kname, "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic}
+    tflops = flop / (linear1_ms * 1e-3) / 1e12
+    return {"bound": "mfma", "kernel": kname, "achieved": round(tflops, 2), "peak": PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(tflops / PEAK_TFLOPS, 4), "traffic": traffic}
+
+
 def load_traffic(cfg_name: str):
     """HBM bytes per Linear1 launch from the committed counter summary, or None if the
     kernel source changed since the counters were taken."""
@@ -313,23 +332,10 @@ def main():
     flop = cfg.flop
     tflops = flop / (ms * 1e-3) / 1e12
     P = cfg.T * cfg.k
-    l1_flop = 4.0 * P * cfg.H * cfg.I
-    l1_tflops = l1_flop / (st_ms[1] * 1e-3) / 1e12
     traffic = load_traffic(cfg.name)
-    # Linear1's algorithmic bytes: W1 and its scales for the experts that receive a row, and
-    # per valid slot its x row, its h8 row and h_sf bytes. Below the ridge (peak FLOP/s over
-    # HBM bytes/s) the launch is priced against HBM bandwidth, else against the MFMA peak.
     ids = inp.topk_idx
-    n_active = int(torch.unique(ids[(ids >= 0) & (ids < cfg.E)]).numel())
-    l1_bytes = w1_bytes * n_active / cfg.E + P * (cfg.H + cfg.I + cfg.I // 128)
-    l1_hbm_bound = l1_flop / l1_bytes < PEAK_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
-    l1_gbs = l1_bytes / (st_ms[1] * 1e-3) / 1e9
-    kname = "Linear1 grouped GEMM with SwiGLU/requant epilogue (main + second launch)"
-    roof = ({"bound": "hbm", "kernel": kname, "achieved": round(l1_gbs, 1), "peak": PEAK_HBM_GBS,
-             "unit": "GB/s", "frac": round(l1_gbs / PEAK_HBM_GBS, 4), "traffic": traffic}
-            if l1_hbm_bound else
-            {"bound": "mfma", "kernel": kname, "achieved": round(l1_tflops, 2), "peak": PEAK_TFLOPS,
-             "unit": "TFLOP/s", "frac": round(l1_tflops / PEAK_TFLOPS, 4), "traffic": traffic})
+    n_active = int(torch.unique(ids[(ids >= 0) & (ids < cfg.E)]).numel())   # experts with a row
+    roof = linear1_roofline(cfg.T, cfg.k, cfg.H, cfg.I, cfg.E, n_active, w1_bytes, float(st_ms[1]), traffic)
     alg_bytes = (w1_bytes + w2_bytes + cfg.T * cfg.H + cfg.T * (4 * ((cfg.H + 511) // 512))
                  + 8 * P + 2 * cfg.T * cfg.H)
     out = {
