@@ -21,9 +21,10 @@ MOE_ERR_ALIGN = -3
 MOE_ERR_WORKSPACE = -4
 MOE_ERR_TOKENS = -5
 MOE_ERR_HIP = -6
+MOE_ERR_SCRATCH = -7
 
 EXPORTED = ("moe_packed_weights_bytes", "moe_prepare_weights", "moe_workspace_bytes",
-            "moe_forward", "moe_forward_events", "moe_workspace_layout", "moe_read_diagnostics",
+            "moe_forward", "moe_forward_events", "moe_forward_noalloc", "moe_workspace_layout", "moe_read_diagnostics",
             "moe_status_string", "moe_version",
             "moe_gemm_packed_b_bytes", "moe_gemm_prepare_b", "moe_gemm_workspace_bytes",
             "moe_fp8_fp4_gemm", "moe_m_grouped_fp8_fp4_gemm_contiguous",
@@ -77,6 +78,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_forward.restype = ctypes.c_int
     lib.moe_forward_events.argtypes = [P, P, P, P, P, I32, shp, P, P, S, P, ctypes.POINTER(P)]
     lib.moe_forward_events.restype = ctypes.c_int
+    lib.moe_forward_noalloc.argtypes = [P, P, P, P, P, I32, shp, P, P]
+    lib.moe_forward_noalloc.restype = ctypes.c_int
     lib.moe_workspace_layout.argtypes = [shp, I32, ctypes.POINTER(moe_layout_t)]
     lib.moe_workspace_layout.restype = ctypes.c_int
     lib.moe_read_diagnostics.argtypes = [shp, P, ctypes.POINTER(I32), ctypes.POINTER(I32), P]
@@ -172,6 +175,27 @@ def moe_forward_events(y, x_fp8, x_sf, topk_idx, topk_weights, num_tokens: int,
         ctypes.byref(shape), _ptr(packed), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream), handles)
     _check(st, "moe_forward_events")
+
+
+# Bytes of the library's fixed scratch array (MOE_NOALLOC_SCRATCH_BYTES in include/moe.h)
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def moe_forward_noalloc(y, x_fp8, x_sf, topk_idx, topk_weights, num_tokens: int,
+                        shape: moe_shape_t, packed, stream=None) -> None:
+    """moe_forward with its workspace in the library's fixed per-GPU scratch array (no
+    workspace argument; calls on one GPU must not overlap)."""
+    st = load_library().moe_forward_noalloc(
+        _ptr(y), _ptr(x_fp8), _ptr(x_sf), _ptr(topk_idx), _ptr(topk_weights), int(num_tokens),
+        ctypes.byref(shape), _ptr(packed), _stream(stream))
+    _check(st, "moe_forward_noalloc")
+
+
+def moe_forward_noalloc_raw(y_ptr, x_ptr, xsf_ptr, idx_ptr, w_ptr, num_tokens, shape, packed_ptr,
+                            stream_ptr) -> int:
+    """Unchecked call with raw integer pointers; returns the status (for error-path tests)."""
+    return load_library().moe_forward_noalloc(y_ptr, x_ptr, xsf_ptr, idx_ptr, w_ptr, int(num_tokens),
+                                              ctypes.byref(shape), packed_ptr, stream_ptr)
 
 
 def _event_handle(ev) -> int:

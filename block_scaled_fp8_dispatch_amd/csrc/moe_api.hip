@@ -4,6 +4,7 @@
 // moe_read_diagnostics, and nothing allocates device memory.
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "moe_internal.h"
 
@@ -111,6 +112,7 @@ const char* moe_status_string(int status) {
         case MOE_ERR_WORKSPACE: return "buffer too small";
         case MOE_ERR_TOKENS: return "num_tokens out of range";
         case MOE_ERR_HIP: return "HIP error";
+        case MOE_ERR_SCRATCH: return "problem exceeds the library's fixed scratch buffer";
         default: return "unknown status";
     }
 }
@@ -273,6 +275,52 @@ int moe_forward_events(uint16_t* y_bf16, const uint8_t* x_fp8, const uint8_t* x_
         if (!events[i]) return MOE_ERR_NULL;
     return forward_impl(y_bf16, x_fp8, x_sf, topk_idx, topk_weights, num_tokens, shape, packed,
                         workspace, workspace_bytes, stream, events);
+}
+
+// Scratch of moe_forward_noalloc: a fixed device array in this library's code object, one
+// copy per GPU, held until the process ends. Host code never passes `scratch` itself to a
+// kernel or a copy (on the host it only names the symbol); it uses the device address that
+// hipGetSymbolAddress returns for the current device, looked up once per device.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (nullptr on a HIP error).
+void* scratch_address() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
+}  // namespace
+
+int moe_forward_noalloc(uint16_t* y_bf16, const uint8_t* x_fp8, const uint8_t* x_sf,
+                        const int32_t* topk_idx, const float* topk_weights, int32_t num_tokens,
+                        const moe_shape_t* shape, const void* packed, hipStream_t stream) {
+    if (!shape) return MOE_ERR_NULL;
+    if (!shape_ok(shape)) return MOE_ERR_SHAPE;
+    if (num_tokens < 0 || num_tokens > shape->max_tokens) return MOE_ERR_TOKENS;
+    if (!y_bf16 || !x_fp8 || !x_sf || !topk_idx || !topk_weights || !packed) return MOE_ERR_NULL;
+    if (!aligned16(y_bf16) || !aligned16(x_fp8) || !aligned16(x_sf) || !aligned16(topk_idx) ||
+        !aligned16(topk_weights) || !aligned16(packed))
+        return MOE_ERR_ALIGN;
+    // the workspace regions sized for this call's tokens, all inside the scratch array
+    moe_shape_t s = *shape;
+    s.max_tokens = num_tokens;
+    if (ws_layout(s).pub.total > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_SCRATCH;
+    if (num_tokens == 0) return MOE_OK;
+    void* ws = scratch_address();
+    if (!ws) return MOE_ERR_HIP;
+    return forward_impl(y_bf16, x_fp8, x_sf, topk_idx, topk_weights, num_tokens, &s, packed, ws,
+                        (size_t)MOE_NOALLOC_SCRATCH_BYTES, stream, nullptr);
 }
 
 int moe_read_diagnostics(const moe_shape_t* shape, const void* workspace, int32_t* invalid_ids,

@@ -27,7 +27,8 @@
  *
  * Memory: every pointer argument is a device pointer, 16-byte aligned, owned by the
  * caller. The library allocates no device memory and holds no global state, so calls
- * on different streams with different workspaces are independent. Every call is
+ * on different streams with different workspaces are independent; the one exception is
+ * moe_forward_noalloc, whose workspace is a fixed array inside the library. Every call is
  * asynchronous on `stream`; outputs are valid once the stream has reached it.
  *
  * Errors: host-detectable problems return a negative status before anything is
@@ -64,7 +65,8 @@ enum {
     MOE_ERR_ALIGN = -3,     /* a pointer is not 16-byte aligned */
     MOE_ERR_WORKSPACE = -4, /* workspace or packed buffer too small */
     MOE_ERR_TOKENS = -5,    /* num_tokens < 0 or > max_tokens */
-    MOE_ERR_HIP = -6        /* a HIP call or kernel launch failed */
+    MOE_ERR_HIP = -6,       /* a HIP call or kernel launch failed */
+    MOE_ERR_SCRATCH = -7    /* moe_forward_noalloc: the call needs more than its fixed scratch */
 };
 
 /* Limits of the shapes this library accepts. */
@@ -120,6 +122,29 @@ int moe_forward_events(uint16_t* y_bf16,
                        int32_t num_tokens, const moe_shape_t* shape, const void* packed,
                        void* workspace, size_t workspace_bytes, hipStream_t stream,
                        hipEvent_t* events);
+
+/* Largest workspace, in bytes, that moe_forward_noalloc can serve from its fixed scratch
+ * array: 64 MiB, which covers decode-sized calls (for instance 256 tokens, 32 experts,
+ * top-8, H = 7168, I = 2048 needs 49 MiB). */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* moe_forward for callers that cannot allocate device memory or size a workspace: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc. Same
+ * arguments and results as moe_forward, without workspace and workspace_bytes: the routing
+ * tables, the FP8 intermediate and the staging rows live in a device array of
+ * MOE_NOALLOC_SCRATCH_BYTES bytes inside the library (one per GPU, held until the process
+ * ends), laid out as moe_workspace_layout gives for a shape with max_tokens = num_tokens.
+ * A call whose layout would need more returns MOE_ERR_SCRATCH before anything is launched.
+ * The call allocates nothing; its first call on a device looks up that device's copy of
+ * the array (hipGetSymbolAddress). Every call on one GPU shares its array, which keeps the
+ * last call's contents (no call needs it cleared): calls that overlap on one GPU (on
+ * different streams without ordering, or from several host threads) race and give wrong
+ * results; order them on one stream or synchronise between them. */
+int moe_forward_noalloc(uint16_t* y_bf16,
+                        const uint8_t* x_fp8, const uint8_t* x_sf,
+                        const int32_t* topk_idx, const float* topk_weights,
+                        int32_t num_tokens, const moe_shape_t* shape, const void* packed,
+                        hipStream_t stream);
 
 /* Where the last moe_forward on `workspace` left its routing tables and
  * intermediates (byte offsets from the workspace base; for tests and tools). */
