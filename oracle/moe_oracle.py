@@ -370,23 +370,21 @@ def forward(x_fp8, x_sf, topk_idx, topk_weights, w1, w1_sf, w2, w2_sf,
       O3  g = x[t] . W1[e, n],  u = x[t] . W1[e, I+n]        (fp64)        [P1 3.1 step 2; 4.2]
       O4  h = silu(g) * u                                                  [P1 3.1 step 3]
       O5  (q, sf) = requant per 1x128 of h; h' = dequant(q, sf)            [P1 11.1]
+    then, on every slot's h' (linear2_combine):
       O6  o = h' . W2[e, m]                                                [P1 3.1 step 4]
       O7  y[t, m] = bf16( sum_j  w[t, j] * o[t, j, m] )                    [P1 3.1 step 5; 9.2]
     """
     x_fp8 = np.asarray(x_fp8)
     T, H = x_fp8.shape
     topk_idx = np.asarray(topk_idx)
-    topk_weights = np.asarray(topk_weights, dtype=np.float32)
     k = topk_idx.shape[1]
     E, twoI, _ = w1.shape
     I = twoI // 2
     assert w2.shape[0] == E and w2.shape[1] == H and w2.shape[2] * 2 == I
     toks = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
-    cols_arr = np.arange(H) if cols is None else np.asarray(cols, dtype=np.int64)
     tok_pos = {int(t): i for i, t in enumerate(toks)}
 
-    contrib = np.zeros((len(toks), k, len(cols_arr)), dtype=np.float64)   # w[t,j] * o[t,j,:]
-    h8, hsf, h64, hbound = {}, {}, {}, {}
+    h8, hsf, hdeq, h64, hbound = {}, {}, {}, {}, {}
     xd_all = dequant_fp8_rows(x_fp8[toks], np.asarray(x_sf)[toks], H)   # [len(toks), H]
     for e in range(E):
         slots = [(int(t), j) for t in toks for j in range(k) if int(topk_idx[t, j]) == e]
@@ -400,6 +398,45 @@ def forward(x_fp8, x_sf, topk_idx, topk_weights, w1, w1_sf, w2, w2_sf,
         h = swiglu(G, U)
         hb = accumulation_error_bound(G, U, AG, AU, H) if keep_bounds else None
         q, sf, hd = requant_fp8_1x128(h)
+        for r, (t, j) in enumerate(slots):
+            hdeq[t * k + j] = hd[r]
+            if keep_intermediates:
+                h8[t * k + j] = q[r]
+                hsf[t * k + j] = sf[r]
+            if keep_bounds:
+                h64[t * k + j] = h[r]
+                hbound[t * k + j] = hb[r]
+    out = linear2_combine(hdeq, topk_idx, topk_weights, w2, w2_sf, tokens=toks, cols=cols,
+                          row_chunk=row_chunk)
+    return dict(y=out["y"], y_bits=out["y_bits"], h8=h8, h_sf=hsf, h=h64, h_bound=hbound,
+                tokens=toks, cols=out["cols"])
+
+
+def linear2_combine(hdeq: Dict[int, np.ndarray], topk_idx, topk_weights, w2, w2_sf,
+                    tokens: Optional[Sequence[int]] = None, cols: Optional[Sequence[int]] = None,
+                    row_chunk: int = 1024):
+    """O6 and O7 on a given requantised intermediate [P1 3.1 steps 4-5; P2 5].
+
+    hdeq: {slot t*k+j: fp64 h' [I]}, the dequantised intermediate of every valid slot of
+    the given tokens (forward() passes its own; a test may pass another device's, decoded
+    exactly). For each valid slot, o = h' . W2[e]^T (fp64); then
+    y[t] = bf16( sum over j = 0..k-1 of w[t, j] * o[t, j] ) in fp64, slot order, skipped
+    slots adding 0. Returns y (fp64 before rounding), y_bits (bf16), cols."""
+    topk_idx = np.asarray(topk_idx)
+    topk_weights = np.asarray(topk_weights, dtype=np.float32)
+    T, k = topk_idx.shape
+    E, H, _ = w2.shape
+    I = 2 * w2.shape[2]
+    toks = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    cols_arr = np.arange(H) if cols is None else np.asarray(cols, dtype=np.int64)
+    tok_pos = {int(t): i for i, t in enumerate(toks)}
+
+    contrib = np.zeros((len(toks), k, len(cols_arr)), dtype=np.float64)   # w[t,j] * o[t,j,:]
+    for e in range(E):
+        slots = [(int(t), j) for t in toks for j in range(k) if int(topk_idx[t, j]) == e]
+        if not slots:
+            continue
+        hd = np.stack([hdeq[t * k + j] for t, j in slots])                 # [R, I]
         O = np.empty((len(slots), len(cols_arr)))                          # [R, len(cols)]
         buf = np.empty((min(row_chunk, len(cols_arr)), I))
         for c0 in range(0, len(cols_arr), row_chunk):
@@ -408,18 +445,11 @@ def forward(x_fp8, x_sf, topk_idx, topk_weights, w1, w1_sf, w2, w2_sf,
             O[:, c0:c0 + len(cc)] = hd @ W2c.T
         for r, (t, j) in enumerate(slots):
             contrib[tok_pos[t], j] = float(topk_weights[t, j]) * O[r]
-            if keep_intermediates:
-                h8[t * k + j] = q[r]
-                hsf[t * k + j] = sf[r]
-            if keep_bounds:
-                h64[t * k + j] = h[r]
-                hbound[t * k + j] = hb[r]
     # O7: the combine sums the slots in order j = 0..k-1 (skipped slots add 0)
     acc = np.zeros((len(toks), len(cols_arr)), dtype=np.float64)
     for j in range(k):
         acc += contrib[:, j]
-    return dict(y=acc, y_bits=bf16_rne_bits(acc), h8=h8, h_sf=hsf, h=h64, h_bound=hbound,
-                tokens=toks, cols=cols_arr)
+    return dict(y=acc, y_bits=bf16_rne_bits(acc), cols=cols_arr)
 
 
 def forward_inputs(inp: dict, **kw):
@@ -434,26 +464,35 @@ def forward_inputs(inp: dict, **kw):
 
 
 def y_row_error(y_bits_gpu: np.ndarray, y_ref: np.ndarray) -> np.ndarray:
-    """Per row: max_m |y_gpu - y_ref| / max_m |y_ref|; rows with y_ref == 0 give 0 only
-    if y_gpu is exactly 0 there (else inf)."""
+    """Per row: max_m |y_gpu - y_ref| / max_m |y_ref| (the largest error in the row over
+    the row's largest reference magnitude). A row whose reference is all zero gives 0 only
+    if y_gpu is exactly zero there (either sign), else inf. A row holding a NaN or an
+    infinity on the GPU side gives inf."""
     yg = bf16_bits_to_f64(y_bits_gpu)
     yr = np.asarray(y_ref, dtype=np.float64)
-    num = np.abs(yg - yr).max(axis=1)
+    bad = ~np.isfinite(yg).all(axis=1)
+    num = np.abs(np.where(np.isfinite(yg), yg, 0.0) - yr).max(axis=1)
     den = np.abs(yr).max(axis=1)
     out = np.where(den > 0, num / np.where(den > 0, den, 1.0), np.where(num == 0, 0.0, np.inf))
-    return out
+    return np.where(bad, np.inf, out)
 
 
 def e4m3_code_distance(a: np.ndarray, sa: np.ndarray, b: np.ndarray, sb: np.ndarray) -> np.ndarray:
     """Distance, in steps of the e4m3 grid at the coarser of the two block scales,
-    between two requantised values (codes a, b with UE8M0 scale bytes sa, sb)."""
-    va = E4M3_TABLE[a] * np.ldexp(1.0, sa.astype(np.int64) - 127)
-    vb = E4M3_TABLE[b] * np.ldexp(1.0, sb.astype(np.int64) - 127)
-    s = np.maximum(sa, sb).astype(np.int64) - 127
-    # re-express both on the coarser scale's grid: position index of value / 2^s
-    ia = _grid_index(va * np.ldexp(1.0, -s))
-    ib = _grid_index(vb * np.ldexp(1.0, -s))
-    return np.abs(ia - ib)
+    between two requantised values (codes a, b with UE8M0 scale bytes sa, sb). A value
+    that lies between two grid points of the coarser scale (a fine-scale subnormal) sits
+    half way between their positions. A NaN code (0x7F, 0xFF) or a NaN scale byte (255)
+    on either side gives inf: such a value is never an acceptable requantisation."""
+    a = np.asarray(a, dtype=np.int64)
+    b = np.asarray(b, dtype=np.int64)
+    sa = np.asarray(sa, dtype=np.int64)
+    sb = np.asarray(sb, dtype=np.int64)
+    invalid = np.isnan(E4M3_TABLE[a]) | np.isnan(E4M3_TABLE[b]) | (sa == 255) | (sb == 255)
+    s = np.maximum(sa, sb) - 127
+    # both values on the coarser scale's grid: e4m3 value times 2^(own scale - coarser scale)
+    ia = _grid_index(np.where(invalid, 0.0, E4M3_TABLE[a]) * np.ldexp(1.0, sa - 127 - s))
+    ib = _grid_index(np.where(invalid, 0.0, E4M3_TABLE[b]) * np.ldexp(1.0, sb - 127 - s))
+    return np.where(invalid, np.inf, np.abs(ia - ib))
 
 
 _POS_VALUES = np.array([e4m3_value(c) for c in range(0x7F)])   # ascending magnitudes 0..448

@@ -13,6 +13,23 @@ OFF_BY_ONE_MAX = 1e-3   # fraction of requantised FP8 intermediates one code off
 # fewest compared intermediates for which that fraction is checked as a rate (at 1e-3, ten
 # expected differences); smaller samples check every difference against the FP32 bound
 RATE_MIN_ELEMENTS = 10_000
+# Reading of "off by one code" for elements far below their block maximum: an element more
+# than one code from the oracle's is excused only if its exact |h| is at most this fraction
+# of its block's largest |h| (at least 4 binades below, where the absolute FP32 error of the
+# block's dot products can exceed the element's own grid step) AND the GPU value is a
+# round-to-nearest result of a value within the FP32 accumulation bound of the exact h
+FAR_BELOW_FRACTION = 2.0 ** -4
+# Most such excused elements a comparison may hold, as a rate of the compared elements
+# (rounded down: fewer than 100 000 compared elements excuse none)
+FAR_EXCUSED_MAX_RATE = 1e-5
+# Reading of the two tolerances together: a one-code difference the intermediate rule
+# accepts (a value within FP32 error of a rounding midpoint) at a block's largest element of
+# a heavily weighted slot moves a y row by up to a few per cent of its largest value. A row
+# whose end-to-end error exceeds Y_TOL therefore passes only if one of its slots holds such
+# an accepted difference and the row is within Y_TOL of the oracle's Linear2 and combine run
+# on the GPU's own (decoded) intermediate; such rows are counted, printed and capped at this
+# rate of the compared rows (rounded up)
+ROW_EXCUSED_MAX_RATE = 1e-3
 
 
 class Run:
@@ -151,17 +168,20 @@ def _e4m3_half_gap() -> np.ndarray:
 _HALF_GAP = _e4m3_half_gap()
 
 
-def check_intermediates(run: Run, ref: dict, inv: np.ndarray):
+def check_intermediates(run: Run, ref: dict, inv: np.ndarray, stats: dict = None):
     """Compare GPU h8/h_sf with the oracle's requantised intermediate slot by slot.
 
-    Each element is decoded on both sides. Each element whose values differ must be one
-    step apart on the e4m3 grid at the coarser of the two block scales, or, where the oracle
-    returns h and its FP32 accumulation error bound, the GPU's value must be a
-    round-to-nearest result of some h' within that bound of the exact h (this covers small
-    elements of a block, where the grid is finer than the FP32 error of a dot product that
-    cancels). With at least RATE_MIN_ELEMENTS elements, the differing ones may be at most
-    0.1 % of them; a smaller sample cannot estimate that rate, and there every differing
-    element must be explained by the FP32 bound instead."""
+    Each element is decoded on both sides and measured on the e4m3 grid of the coarser of
+    the two block scales. An element that differs must be one step apart, with one
+    exception: an element further apart passes only where its exact |h| is at most
+    FAR_BELOW_FRACTION of its block's largest |h| and the GPU's value is a round-to-nearest
+    result of some h' within the FP32 accumulation error bound of the exact h (a dot product
+    that cancels leaves an element whose grid is finer than the FP32 error of the sum).
+    Such excused elements are counted, printed and capped at FAR_EXCUSED_MAX_RATE of the
+    compared elements. With at least RATE_MIN_ELEMENTS elements the differing ones may be
+    at most 0.1 % of them; a smaller sample cannot estimate that rate, and there every
+    differing element must be explained by the FP32 bound instead (the pooled rate of many
+    small samples is checked by the caller from `stats`: n, differing, excused)."""
     slots = sorted(ref["h8"].keys())
     if not slots:
         return 0.0
@@ -173,36 +193,98 @@ def check_intermediates(run: Run, ref: dict, inv: np.ndarray):
     gs = np.repeat(gsf, 128, axis=1)
     rs = np.repeat(rsf, 128, axis=1)
     dist = oracle.e4m3_code_distance(g8, gs, r8, rs)
-    frac = float((dist > 0).mean())
+    assert np.all(np.isfinite(dist)), "a NaN code or a NaN scale byte in the GPU intermediate"
+    n = dist.size
+    n_diff = int((dist > 0).sum())
+    frac = n_diff / n
     far = dist > 1
-    unexplained = np.zeros_like(far)
+    excused = np.zeros_like(far)
+    unexplained = dist > 0
     if ref.get("h"):
         h = np.stack([ref["h"][s] for s in slots])
         hb = np.stack([ref["h_bound"][s] for s in slots])
         scale = np.ldexp(1.0, gs.astype(np.int64) - 127)
         vg = oracle.E4M3_TABLE[g8] * scale
         within = np.abs(vg - h) <= hb + _HALF_GAP[g8] * scale
-        far &= ~within
+        amax = np.repeat(np.abs(h).reshape(h.shape[0], -1, 128).max(axis=2), 128, axis=1)
+        small = np.abs(h) <= FAR_BELOW_FRACTION * amax
+        excused = far & within & small
         unexplained = (dist > 0) & ~within
-    assert not far.any(), (f"{int(far.sum())} intermediates further than one code and outside "
-                           f"the FP32 accumulation bound (max distance {dist.max()})")
-    if dist.size >= RATE_MIN_ELEMENTS:
+    n_far = int(far.sum())
+    n_excused = int(excused.sum())
+    flips = np.nonzero(gsf != rsf)
+    if len(flips[0]):
+        print(f"[intermediates] {len(flips[0])} blocks with a different scale byte: " + ", ".join(
+            f"slot {slots[i]} block {b} gpu {gsf[i, b]} oracle {rsf[i, b]}"
+            for i, b in list(zip(*flips))[:8]), flush=True)
+    cap = int(np.floor(FAR_EXCUSED_MAX_RATE * n))
+    print(f"[intermediates] compared {n}, differing {n_diff} ({frac:.2e}), more than one code "
+          f"apart {n_far} (excused by the FP32 bound far below the block max: {n_excused}, "
+          f"cap {cap})", flush=True)
+    assert n_far == n_excused, (f"{n_far - n_excused} intermediates further than one code and not "
+                                f"excused (max distance {dist.max()})")
+    assert n_excused <= cap, f"{n_excused} excused intermediates exceed the cap {cap}"
+    if n >= RATE_MIN_ELEMENTS:
         assert frac <= OFF_BY_ONE_MAX, f"{frac:.2e} of intermediates differ"
     else:
         # too few elements to estimate a 0.1 % rate: every differing element must instead be
         # explained by FP32 accumulation (a round-to-nearest result of some value within the
         # FP32 accumulation bound of the exact h)
         assert ref.get("h"), "a small sample needs the oracle's accumulation bounds"
-        assert not unexplained.any(), (f"{int(unexplained.sum())} of {dist.size} intermediates "
+        assert not unexplained.any(), (f"{int(unexplained.sum())} of {n} intermediates "
                                        f"differ beyond the FP32 accumulation bound")
+    if stats is not None:
+        stats["n"] = stats.get("n", 0) + n
+        stats["differing"] = stats.get("differing", 0) + n_diff
+        stats["excused"] = stats.get("excused", 0) + n_excused
     return frac
 
 
-def check_y(y_bits: np.ndarray, ref: dict, tokens=None, cols=None):
+def check_y(y_bits: np.ndarray, ref: dict, tokens=None, cols=None, run: Run = None,
+            inv: np.ndarray = None, host: dict = None):
+    """y rows against the oracle: max |y_gpu - y_ref| / max |y_ref| <= Y_TOL per row, a row
+    the oracle gives as exactly zero exactly zero. A row over Y_TOL passes only as described
+    at ROW_EXCUSED_MAX_RATE, which needs the run, the routing's inv and the host inputs.
+    Returns the largest end-to-end row error."""
     yg = y_bits if tokens is None else y_bits[np.asarray(tokens)]
     if cols is not None:
         yg = yg[:, np.asarray(cols)]
     err = oracle.y_row_error(yg, ref["y"])
-    assert np.all(np.isfinite(err)), "a row the oracle gives as exactly 0 is non-zero"
-    assert err.max() <= Y_TOL, f"max row error {err.max():.3e}"
+    rows = np.arange(len(err)) if tokens is None else np.asarray(tokens)
+    worst = np.argsort(err)[::-1][:3]
+    print("[y] worst rows (token: error): " + ", ".join(f"{int(rows[i])}: {err[i]:.3e}" for i in worst),
+          flush=True)
+    assert np.all(np.isfinite(err)), "a non-finite y value, or a row the oracle gives as exactly 0 is non-zero"
+    over = np.nonzero(err > Y_TOL)[0]
+    if len(over):
+        assert run is not None and inv is not None and host is not None, f"max row error {err.max():.3e}"
+        cap = int(np.ceil(ROW_EXCUSED_MAX_RATE * len(err)))
+        assert len(over) <= cap, f"{len(over)} rows over {Y_TOL} (cap {cap}); max {err.max():.3e}"
+        idx = np.asarray(host["topk_idx"])
+        k = idx.shape[1]
+        E = np.asarray(host["w2"]).shape[0]
+        I = 2 * np.asarray(host["w2"]).shape[2]
+        toks = [int(rows[i]) for i in over]
+        slots = [t * k + j for t in toks for j in range(k) if 0 <= int(idx[t, j]) < E]
+        g8, gsf = run.intermediates(inv[np.array(slots)])
+        hdeq = {}
+        for i, sl in enumerate(slots):
+            hdeq[sl] = oracle.dequant_fp8_rows(g8[i:i + 1], gsf[i:i + 1], I)[0]
+        differs = {t: False for t in toks}
+        for i, sl in enumerate(slots):
+            d = oracle.e4m3_code_distance(g8[i], np.repeat(gsf[i], 128), ref["h8"][sl],
+                                          np.repeat(ref["h_sf"][sl], 128))
+            differs[sl // k] |= bool((d > 0).any())
+        assert all(differs.values()), (f"rows over {Y_TOL} with the oracle's own intermediate in "
+                                       f"every slot: {[t for t, v in differs.items() if not v]}")
+        cond = oracle.linear2_combine(hdeq, idx, host["topk_weights"], host["w2"], host["w2_sf"],
+                                      tokens=toks, cols=cols)
+        yo = y_bits[np.array(toks)]
+        if cols is not None:
+            yo = yo[:, np.asarray(cols)]
+        e2 = oracle.y_row_error(yo, cond["y"])
+        print(f"[y] {len(toks)} rows over {Y_TOL} (cap {cap}), each with an accepted intermediate "
+              f"difference; against the oracle's Linear2 and combine on the GPU's intermediate: "
+              + ", ".join(f"{t}: {e:.3e}" for t, e in zip(toks, e2)), flush=True)
+        assert e2.max() <= Y_TOL, f"max row error {e2.max():.3e} on the GPU's own intermediate"
     return float(err.max())

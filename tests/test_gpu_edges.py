@@ -43,7 +43,7 @@ def _parity(run: Run, inp, T=None):
         host[key] = host[key][:T]
     ref = oracle.forward_inputs(host, keep_bounds=True)
     check_intermediates(run, ref, got["inv"])
-    check_y(y, ref)
+    check_y(y, ref, run=run, inv=got["inv"], host=host)
     return y, ref, ref_route
 
 
@@ -168,9 +168,10 @@ def test_half_tiles_of_several_sizes():
         toks.update(int(t) for t in rows[511:513])         # last row of a full tile, first of the half tile
     toks.update(int(t) for t in np.random.default_rng(4).choice(T, 6, replace=False))
     toks = sorted(toks)
-    ref = oracle.forward_inputs(_host(inp), tokens=toks, keep_bounds=True)
+    host = _host(inp)
+    ref = oracle.forward_inputs(host, tokens=toks, keep_bounds=True)
     check_intermediates(run, ref, got["inv"])
-    check_y(y, ref, tokens=toks)
+    check_y(y, ref, tokens=toks, run=run, inv=got["inv"], host=host)
 
 
 @pytest.mark.parametrize("k,BMexp", [(2, 256), (8, 128)])
@@ -289,7 +290,7 @@ def test_offsets_beyond_2gib():
     host = _host(inp)
     ref = oracle.forward_inputs(host, tokens=toks, keep_bounds=True)
     check_intermediates(run, ref, got["inv"])
-    check_y(y, ref, tokens=toks)
+    check_y(y, ref, tokens=toks, run=run, inv=got["inv"], host=host)
 
 
 def test_two_streams_two_workspaces():

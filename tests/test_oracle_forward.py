@@ -44,6 +44,28 @@ def test_closed_form_example(golden_dir):
         assert ro["perm"][int(p)] == s
 
 
+def test_linear2_combine_on_hand_derived_intermediates():
+    """Linear2 and the combine alone, fed the dequantised intermediates the worked example
+    derives by hand (h' = 8192 for slot 0, -8192 for slot 1, -3072 for slot 2), give the
+    example's y; a token subset and a column subset give the matching part of it."""
+    inp = build_closed_form_inputs()
+    hd = {0: np.full(128, 8192.0), 1: np.full(128, -8192.0), 2: np.full(128, -3072.0)}
+    r = oracle.linear2_combine(hd, inp["topk_idx"], inp["topk_weights"], inp["w2"], inp["w2_sf"])
+    assert np.array_equal(r["y_bits"], expected_y_bits())
+    r1 = oracle.linear2_combine({2: hd[2]}, inp["topk_idx"], inp["topk_weights"], inp["w2"],
+                                inp["w2_sf"], tokens=[1], cols=[0, 5])
+    assert r1["y_bits"].tolist() == [[0xC8C0, 0xC840]]
+    # one element of slot 0 one code up (0x79 at scale 2^5: 9216): o_m grows by 1024 * W2[0][m][0],
+    # so y[0, 1] = 524288 + 0.75 * 1024 = 525056, which bf16 (step 4096 there) rounds back to 2^19,
+    # and y[0, 0] = -131072 + 0.75 * 512 = -130688, which rounds to -130560 (step 512 below 2^17)
+    hd1 = dict(hd)
+    hd1[0] = hd[0].copy()
+    hd1[0][0] = 9216.0
+    r2 = oracle.linear2_combine(hd1, inp["topk_idx"], inp["topk_weights"], inp["w2"], inp["w2_sf"])
+    assert r2["y"][0, 0] == -130688.0 and r2["y"][0, 1] == 525056.0
+    assert r2["y_bits"][0, 0] == 0xC7FF and r2["y_bits"][0, 1] == 0x4900
+
+
 def test_closed_form_catches_gate_up_swap_and_nibble_order():
     # the example distinguishes silu(g)*u from silu(u)*g and the nibble order
     inp = build_closed_form_inputs()

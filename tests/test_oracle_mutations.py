@@ -24,6 +24,7 @@ import types
 import pytest
 
 import oracle
+import test_oracle_checkers as P_checkers
 import test_oracle_codecs as P_codecs
 import test_oracle_forward as P_forward
 import test_oracle_gemm as P_gemm
@@ -36,7 +37,7 @@ GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 def _pins():
     """name -> zero-argument callable, one per pin (parametrised pins once per case)."""
     pins = {}
-    for mod in (P_codecs, P_forward, P_gemm, P_route):
+    for mod in (P_checkers, P_codecs, P_forward, P_gemm, P_route):
         short = mod.__name__.replace("test_oracle_", "")
         for name, fn in vars(mod).items():
             if not (name.startswith("test_") and inspect.isfunction(fn)):
@@ -214,8 +215,8 @@ MUTANTS = [
       'forward.test_single_expert_reduces_to_dense_ffn',
       'forward.test_accumulation_error_bound_on_the_path_operands']),
     ('requant_skipped', 'moe_oracle',
-     'O[:, c0:c0 + len(cc)] = hd @ W2c.T',
-     'O[:, c0:c0 + len(cc)] = h @ W2c.T',
+     'hdeq[t * k + j] = hd[r]',
+     'hdeq[t * k + j] = h[r]',
      ['forward.test_single_expert_reduces_to_dense_ffn']),
     ('topk_weight_dropped', 'moe_oracle',
      'contrib[tok_pos[t], j] = float(topk_weights[t, j]) * O[r]',
@@ -283,6 +284,62 @@ MUTANTS = [
      ['gemm.test_gemm_equals_exact_rational_sum',
       'gemm.test_gemm_one_hot_selects_a_column_of_b',
       'gemm.test_fp32_sums_fall_within_the_bound']),
+]
+
+
+# Mistakes in the acceptance metrics every GPU comparison runs through
+CHECKER_PINS = ['checkers.test_code_distance_hand_cases',
+                'checkers.test_code_distance_same_scale_is_rank_difference',
+                'checkers.test_code_distance_across_scales_by_counting']
+MUTANTS += [
+    ('distance_on_finer_scale', 'moe_oracle',
+     's = np.maximum(sa, sb) - 127',
+     's = np.minimum(sa, sb) - 127',
+     ['checkers.test_code_distance_hand_cases',
+      'checkers.test_code_distance_across_scales_by_counting']),
+    ('grid_index_no_half_step', 'moe_oracle',
+     'idx = np.where(exact, i.astype(np.float64), i - 0.5)',
+     'idx = np.where(exact, i.astype(np.float64), i - 1.0)',
+     ['checkers.test_code_distance_hand_cases',
+      'checkers.test_code_distance_across_scales_by_counting']),
+    ('grid_index_half_step_up', 'moe_oracle',
+     'idx = np.where(exact, i.astype(np.float64), i - 0.5)',
+     'idx = np.where(exact, i.astype(np.float64), i + 0.5)',
+     ['checkers.test_code_distance_hand_cases',
+      'checkers.test_code_distance_across_scales_by_counting']),
+    ('grid_index_unsigned', 'moe_oracle',
+     'return np.where(np.signbit(v) & (a > 0), -idx, idx)',
+     'return idx',
+     CHECKER_PINS),
+    ('grid_index_negative_zero_signed', 'moe_oracle',
+     'return np.where(np.signbit(v) & (a > 0), -idx, idx)',
+     'return np.where(np.signbit(v), -idx - 0.5, idx)',
+     ['checkers.test_code_distance_hand_cases',
+      'checkers.test_code_distance_same_scale_is_rank_difference']),
+    ('distance_nan_scale_accepted', 'moe_oracle',
+     ' | (sa == 255) | (sb == 255)',
+     '',
+     ['checkers.test_code_distance_hand_cases']),
+    ('distance_nan_code_accepted', 'moe_oracle',
+     'invalid = np.isnan(E4M3_TABLE[a]) | np.isnan(E4M3_TABLE[b]) |',
+     'invalid =',
+     ['checkers.test_code_distance_hand_cases']),
+    ('y_error_mean_not_max', 'moe_oracle',
+     'num = np.abs(np.where(np.isfinite(yg), yg, 0.0) - yr).max(axis=1)',
+     'num = np.abs(np.where(np.isfinite(yg), yg, 0.0) - yr).mean(axis=1)',
+     ['checkers.test_y_row_error_hand_cases']),
+    ('y_error_mean_denominator', 'moe_oracle',
+     'den = np.abs(yr).max(axis=1)',
+     'den = np.abs(yr).mean(axis=1)',
+     ['checkers.test_y_row_error_hand_cases']),
+    ('y_error_zero_row_lenient', 'moe_oracle',
+     'np.where(num == 0, 0.0, np.inf))',
+     '0.0)',
+     ['checkers.test_y_row_error_hand_cases']),
+    ('y_error_nan_passes', 'moe_oracle',
+     'return np.where(bad, np.inf, out)',
+     'return out',
+     ['checkers.test_y_row_error_hand_cases']),
 ]
 
 
