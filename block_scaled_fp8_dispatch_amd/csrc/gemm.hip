@@ -281,7 +281,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
     // K steps of this workgroup: all of them, or (split-K) the split's range, which starts at
     // a multiple of 4 so that scale words and byte selects line up
     const int k_begin = MODE == 4 ? split * args.ks_split : 0;
-    const int nks = MODE == 4 ? min(args.ks_split, args.K / kBK - k_begin) : args.K / kBK;   // >= 2
+    const int nks = MODE == 4 ? min(args.ks_split, args.K / kBK - k_begin) : args.K / kBK;   // >= 1
 
     // ---- A rows this lane fetches and reads scales for ----------------------------------
     // Every tile load and scale load is a buffer load: 32-bit per-lane offset in a VGPR,
@@ -430,7 +430,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
 #pragma unroll
             for (int j = A_DMA; j < DMA; ++j) dma_one(min(s2, nks - 1), s2, j);
 #pragma unroll
-        for (int j = 0; j < A_DMA; ++j) dma_one(1, 1, j);
+        for (int j = 0; j < A_DMA; ++j) dma_one(min(1, nks - 1), 1, j);
     } else {
 #pragma unroll
         for (int s2 = 1; s2 < DA; ++s2) {
@@ -658,9 +658,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
             // col0 .. col0+FN-1 (the packed W2 interleaves its rows so). Each row is scaled by
             // its slot's top-k weight (Linear2; 1 in the plain GEMM), rounded to bf16 (round
             // to nearest even) and stored as one FN*2-byte chunk per lane into the stage row
-            // of its slot (the plain GEMM: row of D); padding rows are skipped, and in the
-            // plain GEMM so are columns past N (N is a multiple of 16, so a lane's chunk is
-            // wholly in or out). All slot and weight loads are issued before any is needed.
+            // of its slot (the plain GEMM: row of D); padding rows are skipped, and so are
+            // columns past H or N (the last column tile may be partly past them; H is a
+            // multiple of 128 and N of 16, so a lane's chunk is wholly in or out). All slot and weight loads are issued before any is needed.
             typedef float v2f __attribute__((ext_vector_type(2)));
             typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
             const int l = lane & 15;
@@ -680,7 +680,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     wt[fm][r] = MODE == 2 ? args.topk_weights[slot[fm][r] >= 0 ? slot[fm][r] : 0] : 1.0f;
-            const bool col_ok = MODE != 3 || nt * kBN + col0 < args.out_cols;
+            const bool col_ok = nt * kBN + col0 < args.out_cols;
             uint16_t* sbase = args.stage + nt * kBN + col0;
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm) {

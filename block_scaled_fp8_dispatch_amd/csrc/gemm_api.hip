@@ -22,7 +22,7 @@ constexpr int kSplitTargetWorkgroups = 256;
 bool gemm_shape_ok(int G, int N, int K) {
     if (G < 1 || G > MOE_MAX_EXPERTS) return false;
     if (N < 16 || N % 16 != 0) return false;
-    if (K < 256 || K % 128 != 0) return false;
+    if (K < 128 || K % 128 != 0) return false;
     return true;
 }
 

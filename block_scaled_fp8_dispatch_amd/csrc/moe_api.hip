@@ -21,8 +21,8 @@ constexpr int kDispatchCopyMaxTopk = 2;
 bool shape_ok(const moe_shape_t* s) {
     if (!s) return false;
     if (s->num_experts < 1 || s->num_experts > MOE_MAX_EXPERTS) return false;
-    if (s->hidden < 256 || s->hidden % 256 != 0) return false;
-    if (s->intermediate < 256 || s->intermediate % 128 != 0) return false;
+    if (s->hidden < 128 || s->hidden % 128 != 0) return false;
+    if (s->intermediate < 128 || s->intermediate % 128 != 0) return false;
     if (s->num_topk < 1 || s->num_topk > MOE_MAX_TOPK || s->num_topk > s->num_experts) return false;
     if (s->max_tokens < 0) return false;
     const uint64_t slots = (uint64_t)s->max_tokens * (uint64_t)s->num_topk;
@@ -238,7 +238,7 @@ static int forward_impl(uint16_t* y_bf16, const uint8_t* x_fp8, const uint8_t* x
     a2.a_stride = I;
     a2.a_sf_stride = (int)W.pub.h_sf_stride;
     a2.K = I;
-    a2.n_tiles = H / 256;
+    a2.n_tiles = cdiv(H, 256);   // a last tile of 128 columns when H is an odd multiple of 128
     a2.b = pk + L.w2d;
     a2.b_sf = reinterpret_cast<const uint32_t*>(pk + L.w2s);
     a2.b_expert = L.w2d_expert;

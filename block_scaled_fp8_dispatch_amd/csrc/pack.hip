@@ -21,10 +21,11 @@
 // fragment f is row 128*(f/8) + 8*j + f%8, so a wave owning fragments 8w..8w+7 (or
 // 4w..4w+3) holds 8 (or 4) consecutive output columns per lane.
 //   W1 scales [E][I/128][ceil(H/512)][16][64] u32
-//   W2 data   [E][H/256][I/128][16][64][16 B]             256 rows of H per column tile
-//   W2 scales [E][H/256][ceil(I/512)][16][64] u32
+//   W2 data   [E][ceil(H/256)][I/128][16][64][16 B]       256 rows of H per column tile
+//   W2 scales [E][ceil(H/256)][ceil(I/512)][16][64] u32
 // Every byte of the input lands in exactly one place; scale bytes of K steps past the
-// end of K are zero.
+// end of K are zero. When H is an odd multiple of 128, W2's last column tile is completed
+// with 128 zero rows (data and scale bytes 0), as B of the plain GEMMs below.
 //
 // The plain GEMMs' B ([G][N][K], section 4.3 of the same page) takes the W2 layout with N
 // in place of H; when N is not a multiple of 256 the last column tile is completed with
@@ -102,7 +103,7 @@ PackedLayout packed_layout(const moe_shape_t& s) {
     PackedLayout L{};
     const size_t E = s.num_experts, H = s.hidden, I = s.intermediate;
     const size_t nks1 = H / 128, nkb1 = (H + 511) / 512, nb1 = I / 128;
-    const size_t nks2 = I / 128, nkb2 = (I + 511) / 512, nt2 = H / 256;
+    const size_t nks2 = I / 128, nkb2 = (I + 511) / 512, nt2 = (H + 255) / 256;
     L.w1d_ntile = nks1 * kBTileBytes;
     L.w1d_expert = nb1 * L.w1d_ntile;
     L.w1s_ntile = nkb1 * kBScaleBlockBytes;
@@ -125,7 +126,7 @@ hipError_t launch_pack(const moe_shape_t& s, const PackedLayout& L, const uint8_
                        uint8_t* packed, hipStream_t stream) {
     const int E = s.num_experts, H = s.hidden, I = s.intermediate;
     const int nks1 = H / 128, nkb1 = cdiv(H, 512), nb1 = I / 128;
-    const int nks2 = I / 128, nkb2 = cdiv(I, 512), nt2 = H / 256;
+    const int nks2 = I / 128, nkb2 = cdiv(I, 512), nt2 = cdiv(H, 256);
     const int T = 256;
     {
         const size_t n = (size_t)E * nb1 * nks1 * 1024;

@@ -26,7 +26,7 @@
  * low nibble of byte i, [G][N][K/2]; its scales are UE8M0 per 1x32 block along K,
  * [G][N][K/32]. D is bf16: the FP32 sum of the products, rounded to nearest even.
  *
- * Shapes: K a multiple of 128 and at least 256; N a multiple of 16 and at least 16;
+ * Shapes: K a positive multiple of 128; N a multiple of 16 and at least 16;
  * G (groups) in [1, MOE_MAX_EXPERTS]; the rows of A times K below 2^32.
  *
  * Memory, errors and streams as in moe.h: device pointers, 16-byte aligned, owned by the

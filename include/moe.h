@@ -47,9 +47,12 @@
 extern "C" {
 #endif
 
-/* Problem shape. num_experts = E local experts; hidden = H (multiple of 256);
- * intermediate = I (multiple of 128, at least 256); num_topk = k (1..64); max_tokens = the largest
- * num_tokens a workspace must serve (the capacity of the pages' per-rank buffer). */
+/* Problem shape. num_experts = E local experts (1..1024); hidden = H and intermediate = I,
+ * each a positive multiple of 128 (one 1x128 activation scale block; the pages' block
+ * granularity, chenxutan.com/d/1930 section 11.1); num_topk = k (1..min(64, E));
+ * max_tokens = the largest num_tokens a workspace must serve (the capacity of the pages'
+ * per-rank buffer, section 3.3). Shapes whose byte offsets would not fit the kernels' 32-bit
+ * offsets are refused (MOE_ERR_SHAPE). */
 typedef struct {
     int32_t num_experts;
     int32_t hidden;
@@ -74,7 +77,11 @@ enum {
 #define MOE_MAX_TOPK 64
 
 /* Bytes of the packed weight buffer for `shape` (W1 and W2 with their scales, in the
- * kernels' fragment order). Returns 0 if the shape is unsupported. */
+ * kernels' fragment order): the destination of the one-time weight transform that the
+ * pages' call sequence runs before any forward (chenxutan.com/d/1930 section 3.3,
+ * transform_weights_for_mega_moe). The input's byte count, plus W2's last 256-row column
+ * tile completed with zero rows when H is an odd multiple of 128. Returns 0 if the shape
+ * is unsupported. */
 size_t moe_packed_weights_bytes(const moe_shape_t* shape);
 
 /* Weight transform (the pages' transform_weights_for_mega_moe, chenxutan.com/d/1930
@@ -92,7 +99,11 @@ int moe_prepare_weights(const moe_shape_t* shape,
                         void* packed, size_t packed_bytes, hipStream_t stream);
 
 /* Bytes of the workspace `moe_forward` needs for up to shape->max_tokens tokens
- * (routing tables, FP8 intermediate with its scales, per-slot bf16 staging). */
+ * (routing tables, FP8 intermediate with its scales, per-slot bf16 staging): the analogue
+ * of the per-rank buffer the pages size from (E, max tokens, k, H, I) before the first
+ * forward (chenxutan.com/d/1930 section 3.3, get_symm_buffer_for_mega_moe), without the
+ * symmetric-memory part, since one GPU exchanges nothing. Returns 0 if the shape is
+ * unsupported. */
 size_t moe_workspace_bytes(const moe_shape_t* shape);
 
 /* The forward (the pages' fp8_fp4_mega_moe, chenxutan.com/d/1930 section 3.3).

@@ -52,9 +52,19 @@ def test_sizes_and_shape_validation(lib):
     for bad in (moe.make_shape(0, 256, 128, 1, 1), moe.make_shape(4, 200, 128, 1, 1),
                 moe.make_shape(4, 256, 100, 1, 1), moe.make_shape(4, 256, 128, 5, 1),
                 moe.make_shape(4, 256, 128, 0, 1), moe.make_shape(4, 256, 128, 1, -1),
-                moe.make_shape(2000, 256, 128, 1, 1), moe.make_shape(4, 256, 128, 65, 100)):
+                moe.make_shape(2000, 256, 128, 1, 1), moe.make_shape(4, 256, 128, 65, 100),
+                moe.make_shape(4, 64, 128, 1, 1), moe.make_shape(4, 128, 0, 1, 1)):
         assert moe.moe_packed_weights_bytes(bad) == 0
         assert moe.moe_workspace_bytes(bad) == 0
+    # H and I need only be multiples of 128; with H an odd multiple of 128, W2's last column
+    # tile of 256 rows is completed with zero rows
+    for E, H, I in ((4, 128, 128), (4, 384, 128), (3, 640, 384)):
+        nb = moe.moe_packed_weights_bytes(moe.make_shape(E, H, I, 2, 64))
+        h_pad = -(-H // 256) * 256
+        w1 = E * (2 * I * H // 2 + I // 128 * (-(-H // 512)) * 16 * 64 * 4)
+        w2 = E * (h_pad * I // 2 + h_pad // 256 * (-(-I // 512)) * 16 * 64 * 4)
+        assert w1 + w2 <= nb < w1 + w2 + 4 * 256, (E, H, I)
+        assert moe.moe_workspace_bytes(moe.make_shape(E, H, I, 2, 64)) > 0
 
 
 def test_layout_is_consistent(lib):
@@ -136,7 +146,7 @@ def test_gemm_sizes_and_host_errors(lib):
     nb = moe.moe_gemm_packed_b_bytes(G, N, K)
     # N padded to 9 tiles of 256 rows: FP4 data + one 32-bit scale word per lane, fragment and 512 K
     assert nb == G * 9 * 256 * K // 2 + G * 9 * ((K + 511) // 512) * 16 * 64 * 4
-    for bad in ((0, 256, 256), (1025, 256, 256), (1, 8, 256), (1, 264, 256), (1, 256, 128),
+    for bad in ((0, 256, 256), (1025, 256, 256), (1, 8, 256), (1, 264, 256), (1, 256, 64),
                 (1, 256, 320)):
         assert moe.moe_gemm_packed_b_bytes(*bad) == 0
     assert moe.moe_gemm_workspace_bytes(-1, 1) == 0 and moe.moe_gemm_workspace_bytes(10, 0) == 0

@@ -76,7 +76,8 @@ def _check_rows(d, rows, ref_rows, ref):
 @pytest.mark.parametrize("cfg", [
     GEMM_CONFIGS["g_tiny"],                                           # ragged M and N, K = 3 steps
     GemmConfig("g_mid", "dense", M=1000, N=528, K=1152),              # 256-row tiles + tail halves
-    GemmConfig("g_one", "dense", M=1, N=16, K=256),                   # smallest shape
+    GemmConfig("g_one", "dense", M=1, N=16, K=128),                   # smallest shape: one K step
+    GemmConfig("g_k128", "dense", M=300, N=272, K=128),               # one K step, 128-row tiles
     GemmConfig("g_split128", "dense", M=200, N=1040, K=4096),         # split K, 128-row tiles
     GEMM_CONFIGS["g_dense_decode"],                                   # split K, 64-row tiles
 ], ids=lambda c: c.name)

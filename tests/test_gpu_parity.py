@@ -3,8 +3,8 @@
 Routing/permutation/counts/tile list: bit-exact. Requantised FP8 intermediates: at most
 0.1 % differ, each by one code on the e4m3 grid of the coarser block scale; an element more
 than one code off passes only if it lies at most 1/16 of its block's largest |h| and is
-explained by the FP32 accumulation bound, and such elements are capped at a rate of 1e-5
-(gpu_helpers.check_intermediates). Samples under 10 000 elements, too small to estimate a
+explained by the FP32 accumulation bound, and such elements are capped at a rate of 1e-5,
+rounded up (gpu_helpers.check_intermediates). Samples under 10 000 elements, too small to estimate a
 0.1 % rate, need every difference explained by the FP32 bound, and their pooled rate is
 checked over the whole tiny-shape sweep. y: max |y_gpu - y_ref| / max |y_ref| <= 2e-2 per
 row, rows the oracle gives as exactly 0 are exactly 0.
@@ -20,8 +20,8 @@ pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
 
 import oracle  # noqa: E402
-from gpu_helpers import (OFF_BY_ONE_MAX, RATE_MIN_ELEMENTS, Run, check_intermediates,  # noqa: E402
-                         check_routing, check_y)
+from gpu_helpers import (FAR_EXCUSED_MAX_RATE, OFF_BY_ONE_MAX, RATE_MIN_ELEMENTS, Run,  # noqa: E402
+                         check_intermediates, check_routing, check_y)
 
 
 def _full_check(cfg: MoEConfig, seed=0, tokens=None, cols=None, max_tokens=None, stats=None):
@@ -52,6 +52,11 @@ def test_tiny_c0():
     (700, 3, 2, 256, 640, 2),      # medium class, I not a multiple of 512
     (1200, 2, 2, 768, 256, 3),     # large class, K steps not a multiple of 4
     (1, 4, 2, 256, 256, 4),        # one token
+    (200, 3, 2, 384, 128, 6),      # H an odd multiple of 128 (Linear2's last column tile half
+                                   # empty), I = 128 (Linear2 has one K step)
+    (40, 2, 2, 128, 256, 7),       # H = 128: Linear1 has one K step, Linear2 one half tile
+    (1100, 2, 2, 640, 384, 8),     # 256-row tiles and second launch with H = 640
+    (300, 4, 3, 128, 128, 9),      # H = I = 128 with rows read through the row list (top-3)
 ])
 def test_small_shapes(T, E, k, H, I, seed):
     _full_check(MoEConfig("small", T=T, E=E, k=k, H=H, I=I), seed=seed)
@@ -80,4 +85,4 @@ def test_tiny_shape_sweep_pooled_rate():
           f"({rate:.2e}); excused far elements {stats['excused']}", flush=True)
     assert stats["n"] >= RATE_MIN_ELEMENTS
     assert rate <= OFF_BY_ONE_MAX
-    assert stats["excused"] == 0
+    assert stats["excused"] <= int(np.ceil(FAR_EXCUSED_MAX_RATE * stats["n"]))
