@@ -17,7 +17,8 @@ the FP8 cast of 8192 x 7168 bf16 rows.
 Prints one JSON line. FLOP = 6*T*k*H*I over valid slots only (2*P*H*2I for Linear1 plus
 2*P*I*H for Linear2). Stage times come from HIP events the library records on the
 launch stream between its kernels; the roofline object is for Linear1, the dominant
-kernel. The CPU baseline is the oracle (numpy fp64) timed on a bounded token sample.
+kernel. The CPU baseline is the plain C++ fp64 oracle timed on a bounded token sample,
+with the host's CPU model and core counts.
 """
 from __future__ import annotations
 
@@ -46,7 +47,7 @@ def parse():
     ap.add_argument("--config", default="c2")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=128)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this size first (for counter scaling)")
     return ap.parse_args()
@@ -98,27 +99,57 @@ def load_traffic(cfg_name: str):
     return float(m_bytes.group(1))
 
 
-def cpu_baseline(inp_cpu: dict, cfg, n_tokens: int):
-    """Time the oracle on the first n_tokens tokens of the batch (every expert they route to
-    is decoded, so the sample carries the oracle's full per-expert cost)."""
-    import numpy as np
-    import oracle
+def host_cpu():
+    """The host's CPU model, physical cores, logical CPUs, and the CPUs this process may run
+    on (its affinity, capped by OMP_NUM_THREADS where that is set)."""
+    model, cores = "unknown", set()
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
-    except Exception:
-        threads = os.cpu_count() or 1
+        phys = core = None
+        for line in open("/proc/cpuinfo"):
+            key, _, val = line.partition(":")
+            key, val = key.strip(), val.strip()
+            if key == "model name" and model == "unknown":
+                model = val
+            elif key == "physical id":
+                phys = val
+            elif key == "core id":
+                core = val
+            elif not key and phys is not None:
+                cores.add((phys, core))
+                phys = core = None
+        if phys is not None:
+            cores.add((phys, core))
+    except OSError:
+        pass
+    logical = os.cpu_count() or 1
+    usable = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else logical
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        usable = min(usable, int(omp))
+    return model, len(cores) or None, logical, usable
+
+
+def cpu_baseline(inp_cpu: dict, cfg, n_tokens: int):
+    """Time the plain C++ oracle (oracle/ref_forward.cpp: fp64, one ascending sum per dot
+    product, std::thread over output rows, timed inside with std::chrono::steady_clock) on
+    the first n_tokens tokens of the batch, with one thread per CPU this process may use.
+    Every expert the sample routes to is decoded, so the sample carries the oracle's full
+    per-expert cost."""
+    import numpy as np
+    from oracle import ref_cpp
+    model, phys, logical, usable = host_cpu()
     idx = inp_cpu["topk_idx"]
     toks = list(range(min(n_tokens, idx.shape[0])))
-    t0 = time.perf_counter()
-    oracle.forward_inputs(inp_cpu, tokens=toks)
-    dt = time.perf_counter() - t0
-    slots = int(np.sum((idx[toks] >= 0) & (idx[toks] < cfg.E)))
-    experts = int(len(np.unique(idx[toks][(idx[toks] >= 0) & (idx[toks] < cfg.E)])))
+    r = ref_cpp.forward_cpp(inp_cpu, tokens=toks, threads=usable, keep_intermediates=False)
+    dt = r["seconds"]
+    valid = (idx[toks] >= 0) & (idx[toks] < cfg.E)
+    slots = int(np.sum(valid))
+    experts = int(len(np.unique(idx[toks][valid])))
     flop = 6.0 * slots * cfg.H * cfg.I
-    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(r["threads"]), "kind": "oracle",
             "sample": f"first {len(toks)} tokens ({slots} slots over {experts} experts) of {cfg.name}, "
-                      f"{dt:.1f} s; numpy fp64, BLAS threads={threads}",
+                      f"{dt:.1f} s; plain C++ fp64 oracle (no BLAS), {r['threads']} std::thread workers",
+            "cpu_model": model, "physical_cores": phys, "logical_cpus": logical,
             "seconds": dt}
 
 

@@ -70,3 +70,22 @@ def test_roofline_counts_only_experts_that_receive_rows():
     P = c.T * c.k
     expect = _w1_bytes(c) / 2 + P * (c.H + c.I + c.I // 128)
     assert half["achieved"] == pytest.approx(expect / 1e-3 / 1e9, rel=1e-4)
+
+
+def test_host_cpu_description():
+    model, phys, logical, usable = bench.host_cpu()
+    assert isinstance(model, str) and model
+    assert logical >= 1 and 1 <= usable <= logical
+    assert phys is None or 1 <= phys <= logical
+
+
+def test_cpu_baseline_times_the_cpp_oracle():
+    """The baseline leg runs the plain C++ oracle on the first tokens of a batch and reports
+    its rate, the threads it used and the host's CPU (tiny workload, a few tokens)."""
+    from synth import make_inputs
+    cfg = CONFIGS["c0"]
+    host = make_inputs(cfg, seed=0).numpy()
+    cb = bench.cpu_baseline(host, cfg, 8)
+    assert cb["kind"] == "oracle" and cb["unit"] == "TFLOP/s" and cb["value"] > 0
+    assert cb["cores"] >= 1 and cb["cpu_model"]
+    assert "first 8 tokens" in cb["sample"] and "C++" in cb["sample"]
