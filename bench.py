@@ -15,8 +15,9 @@ GEMM; the shapes of juejin.cn/post/7631516744872673307 "性能实测"), and --co
 the FP8 cast of 8192 x 7168 bf16 rows.
 
 Prints one JSON line. FLOP = 6*T*k*H*I over valid slots only (2*P*H*2I for Linear1 plus
-2*P*I*H for Linear2). Stage times come from HIP events the library records on the
-launch stream between its kernels; the roofline object is for Linear1, the dominant
+2*P*I*H for Linear2). The timed region holds K plain forwards between two events on the
+launch stream; stage times come from a separate loop of forwards whose HIP events the
+library records between its kernels; the roofline object is for Linear1, the dominant
 kernel. The CPU baseline is the plain C++ fp64 oracle timed on a bounded token sample,
 with the host's CPU model and core counts.
 """
@@ -47,7 +48,7 @@ def parse():
     ap.add_argument("--config", default="c2")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=128)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=384)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this size first (for counter scaling)")
     return ap.parse_args()
@@ -339,24 +340,37 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
+    # The timed region: K plain forwards between two events on the launch stream. The stage
+    # split and the per-step spread come from two further loops of K forwards, so that no
+    # event other than the two brackets sits inside the timed forwards (at T=128 the five
+    # stage events of moe_forward_events add about 20 us to a 157 us forward).
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
-    for row in evs:          # create the HIP events before the timed region
-        for e in row:
-            e.record()
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    for e in [e for row in evs for e in row] + marks:   # create the HIP events beforehand
+        e.record()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record()
     for i in range(K):
-        step(evs[i])
+        step()
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     total_ms = start.elapsed_time(end)
     ms = total_ms / K
+    # per-step spread: one event between consecutive forwards
+    marks[0].record()
+    for i in range(K):
+        step()
+        marks[i + 1].record()
+    # stage split: the library records its stage events between its own launches
+    for i in range(K):
+        step(evs[i])
+    torch.cuda.synchronize()
+    per_step = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(K)])
     stage = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(4)] for i in range(K)])
     st_ms = stage.mean(axis=0)
-    per_step = np.array([evs[i][0].elapsed_time(evs[i][4]) for i in range(K)])   # first to last stage event
     yv = y.view(torch.bfloat16).float()
     assert torch.isfinite(yv).all().item(), "non-finite output"
 
