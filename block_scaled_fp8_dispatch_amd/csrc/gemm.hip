@@ -7,9 +7,9 @@
 //     x packed W1 of the row tile's expert; the epilogue applies SwiGLU (step 3) and
 //     requantises h to e4m3 with one UE8M0 scale per 1x128 block (section 11.1's per-block
 //     amax scaling, rounded up to a power of two).
-//   Linear2 (step 4): rows of h8 x packed W2; the epilogue multiplies each row by its
-//     top-k weight and writes it, as bf16, to the staging row of its (token, slot) (the
-//     combine of step 5 then sums a token's slots in slot order, without atomics).
+//   Linear2 (step 4): rows of h8 x packed W2; the epilogue writes each row, as bf16, to the
+//     staging row of its (token, slot) (the combine of step 5 then weights a token's slots
+//     by their top-k weights and sums them in slot order, without atomics).
 //   Plain GEMM (section 4.3's FP8 x FP4 GEMM, and its M-grouped contiguous and masked
 //     forms): rows of A named by the row list x packed B of the tile's group; the epilogue
 //     writes each row, as bf16, to the same row of D, skipping columns past N. With few
@@ -655,19 +655,18 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
             }
         } else {
             // Lane column l of the wave's fragments wn*FN .. wn*FN+FN-1 holds output columns
-            // col0 .. col0+FN-1 (the packed W2 interleaves its rows so). Each row is scaled by
-            // its slot's top-k weight (Linear2; 1 in the plain GEMM), rounded to bf16 (round
-            // to nearest even) and stored as one FN*2-byte chunk per lane into the stage row
-            // of its slot (the plain GEMM: row of D); padding rows are skipped, and so are
-            // columns past H or N (the last column tile may be partly past them; H is a
-            // multiple of 128 and N of 16, so a lane's chunk is wholly in or out). All slot and weight loads are issued before any is needed.
+            // col0 .. col0+FN-1 (the packed W2 interleaves its rows so). Each row is rounded to
+            // bf16 (round to nearest even) and stored as one FN*2-byte chunk per lane into the
+            // stage row of its slot (the plain GEMM: row of D); the combine applies the top-k
+            // weights. Padding rows are skipped, and so are columns past H or N (the last
+            // column tile may be partly past them; H is a multiple of 128 and N of 16, so a
+            // lane's chunk is wholly in or out). All slot loads are issued before any is needed.
             typedef float v2f __attribute__((ext_vector_type(2)));
             typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
             const int l = lane & 15;
             const int fw = wn * FN;
             const int col0 = 128 * (fw >> 3) + 8 * l + (fw & 7);
             int slot[FM][4];
-            float wt[FM][4];
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
@@ -675,11 +674,6 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
                     const int row = row0 + wm * WM + fm * 16 + 4 * g + r;
                     slot[fm][r] = dense ? (row < args.dense_rows ? row : -1) : args.perm[row];
                 }
-#pragma unroll
-            for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    wt[fm][r] = MODE == 2 ? args.topk_weights[slot[fm][r] >= 0 ? slot[fm][r] : 0] : 1.0f;
             const bool col_ok = nt * kBN + col0 < args.out_cols;
             uint16_t* sbase = args.stage + nt * kBN + col0;
 #pragma unroll
@@ -689,7 +683,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
                     uint32_t pk[FN / 2];
 #pragma unroll
                     for (int p = 0; p < FN / 2; ++p) {
-                        const v2f x = {acc[fm][2 * p][r] * wt[fm][r], acc[fm][2 * p + 1][r] * wt[fm][r]};
+                        const v2f x = {acc[fm][2 * p][r], acc[fm][2 * p + 1][r]};
                         pk[p] = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, v2bf));
                     }
                     if (slot[fm][r] >= 0 && col_ok) {

@@ -251,8 +251,8 @@ static int forward_impl(uint16_t* y_bf16, const uint8_t* x_fp8, const uint8_t* x
     if (launch_linear2(BM, a2, stream) != hipSuccess) return MOE_ERR_HIP;
     if (mark(3) != hipSuccess) return MOE_ERR_HIP;
 
-    if (launch_combine(reinterpret_cast<const uint16_t*>(ws + W.pub.stage), topk_idx, T, k, E, H,
-                       y_bf16, stream) != hipSuccess)
+    if (launch_combine(reinterpret_cast<const uint16_t*>(ws + W.pub.stage), topk_idx, topk_weights,
+                       T, k, E, H, y_bf16, stream) != hipSuccess)
         return MOE_ERR_HIP;
     if (mark(4) != hipSuccess) return MOE_ERR_HIP;
     return MOE_OK;

@@ -155,7 +155,7 @@ hipError_t launch_gather(const uint8_t* x, const uint8_t* x_sf, const int32_t* p
                          uint8_t* xg, uint8_t* xg_sf, hipStream_t stream);
 
 // Combine (combine.hip)
-hipError_t launch_combine(const uint16_t* stage, const int32_t* topk_idx, int T, int k, int E,
-                          int H, uint16_t* y, hipStream_t stream);
+hipError_t launch_combine(const uint16_t* stage, const int32_t* topk_idx, const float* topk_weights,
+                          int T, int k, int E, int H, uint16_t* y, hipStream_t stream);
 
 }  // namespace moe

@@ -124,7 +124,7 @@ int moe_forward(uint16_t* y_bf16,
 
 /* moe_forward, also recording five caller-created events on `stream` at the stage
  * boundaries: events[0] before dispatch, [1] after dispatch, [2] after Linear1 (with its
- * SwiGLU/requant epilogue), [3] after Linear2 (with its weighting epilogue), [4] after
+ * SwiGLU/requant epilogue), [3] after Linear2, [4] after
  * the combine. For per-stage timing with hipEventElapsedTime; nothing synchronises.
  * events must point to 5 valid hipEvent_t; other arguments as for moe_forward. */
 int moe_forward_events(uint16_t* y_bf16,
