@@ -57,6 +57,7 @@ namespace moe {
 namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
@@ -180,7 +181,7 @@ struct Cfg {
 // ABLK: A in the blocked layout (Linear2's h8, Linear1's dispatch copy); otherwise A rows are
 // read through the row list. The forward's GEMMs (MODE 1, 2) read A's scales from the blocked
 // scale copy (h_sf, xg_sf); the plain GEMMs read them row by row.
-template <int BM, int WAVES_M, int WAVES_N, int MODE, bool ABLK>
+template <int BM, int WAVES_M, int WAVES_N, int MODE, bool ABLK, bool OUT32>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args) {
     // The body uses gfx950 buffer descriptors, a device-only type: the host pass of the
     // split compilation sees an empty kernel and emits only its launch stub.
@@ -296,6 +297,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
     // stored); in the plain GEMM perm names A rows directly.
     constexpr bool blocked = ABLK;
     static_assert(!ABLK || MODE <= 2, "blocked A: the forward's GEMMs only");
+    static_assert(!OUT32 || MODE == 2, "32-bit output offsets: Linear2 only");
     constexpr bool sblk = MODE <= 2;   // A scales in the blocked scale layout
     static_assert(!sblk || (FM % 4 == 0 && WM % 64 == 0), "scale words of 4 fragments per load");
     const int NKB = args.K / kBK;
@@ -676,6 +678,15 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
                 }
             const bool col_ok = nt * kBN + col0 < args.out_cols;
             uint16_t* sbase = args.stage + nt * kBN + col0;
+            // OUT32 (Linear2 with a staging buffer of less than 4 GiB): buffer stores at 32-bit
+            // byte offsets, a padding row or a column past the end sent to an offset past the
+            // descriptor's range, where the store is dropped; no 64-bit address arithmetic and
+            // no branch per row (c4: about -1 %). Otherwise 64-bit addresses, padding rows
+            // branched around.
+            const uint32_t out_limit = args.out_bytes;
+            const uint32_t row_bytes = 2u * (uint32_t)args.out_cols;
+            const uint32_t col_byte = 2u * (uint32_t)(nt * kBN + col0);
+            const __amdgpu_buffer_rsrc_t rs_out = __builtin_amdgcn_make_buffer_rsrc(args.stage, 0, (int)out_limit, kRsrcWord3);
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm) {
 #pragma unroll
@@ -686,7 +697,16 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
                         const v2f x = {acc[fm][2 * p][r], acc[fm][2 * p + 1][r]};
                         pk[p] = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, v2bf));
                     }
-                    if (slot[fm][r] >= 0 && col_ok) {
+                    if constexpr (OUT32) {
+                        const uint32_t off = slot[fm][r] >= 0 && col_ok
+                                                 ? (uint32_t)slot[fm][r] * row_bytes + col_byte
+                                                 : out_limit;
+                        if constexpr (FN == 8)
+                            __builtin_amdgcn_raw_buffer_store_b128((v4i){(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3]},
+                                                                   rs_out, off, 0, 0);
+                        else
+                            __builtin_amdgcn_raw_buffer_store_b64((v2u){pk[0], pk[1]}, rs_out, off, 0, 0);
+                    } else if (slot[fm][r] >= 0 && col_ok) {
                         uint16_t* dst = sbase + (size_t)slot[fm][r] * args.out_cols;
                         if constexpr (FN == 8)
                             *reinterpret_cast<v4i*>(dst) = (v4i){(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3]};
@@ -750,17 +770,17 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
     *reinterpret_cast<uint2*>(d + (size_t)out_row * N + col) = make_uint2(lo, hi);
 }
 
-template <int BM, int WAVES_M, int WAVES_N, int MODE, bool ABLK>
+template <int BM, int WAVES_M, int WAVES_N, int MODE, bool ABLK, bool OUT32>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
     // one workgroup per possible tile; those past the tiles in use return at once
     const unsigned grid = (unsigned)a.max_tiles * (unsigned)a.n_tiles;
-    grouped_gemm_kernel<BM, WAVES_M, WAVES_N, MODE, ABLK><<<grid, kThreads, 0, stream>>>(a);
+    grouped_gemm_kernel<BM, WAVES_M, WAVES_N, MODE, ABLK, OUT32><<<grid, kThreads, 0, stream>>>(a);
     return hipGetLastError();
 }
 
 // Workgroups of a kernel the current device runs at once (CUs x workgroups per CU),
 // computed once per device; 0 if unknown.
-template <int BM, int WAVES_M, int WAVES_N, int MODE, bool ABLK>
+template <int BM, int WAVES_M, int WAVES_N, int MODE, bool ABLK, bool OUT32>
 int resident_workgroups() {
     static int cached[64] = {0};
     int dev = 0;
@@ -769,7 +789,7 @@ int resident_workgroups() {
         int cus = 0, per_cu = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &per_cu, grouped_gemm_kernel<BM, WAVES_M, WAVES_N, MODE, ABLK>, kThreads, 0) != hipSuccess)
+                &per_cu, grouped_gemm_kernel<BM, WAVES_M, WAVES_N, MODE, ABLK, OUT32>, kThreads, 0) != hipSuccess)
             return 0;
         cached[dev] = cus * (per_cu > 0 ? per_cu : 1);
     }
@@ -780,15 +800,15 @@ int resident_workgroups() {
 // waves of 64x128, 64 rows as 1x4 waves of 64x64. The 256-row class leaves a last round
 // that would be at most half full to a 128-row launch over tile halves (the tile count
 // is known only on the device, so that launch always goes out and finds its share).
-template <int MODE, bool ABLK>
+template <int MODE, bool ABLK, bool OUT32>
 hipError_t launch_mode(int block_m, const GemmArgs& a, hipStream_t stream) {
     if (a.max_tiles == 0 || a.n_tiles == 0) return hipSuccess;
     switch (block_m) {
         case 256: {
             GemmArgs m = a;
-            m.split_round = resident_workgroups<256, 2, 2, MODE, ABLK>();
+            m.split_round = resident_workgroups<256, 2, 2, MODE, ABLK, OUT32>();
             m.tail = 0;
-            hipError_t e = launch_cfg<256, 2, 2, MODE, ABLK>(m, stream);
+            hipError_t e = launch_cfg<256, 2, 2, MODE, ABLK, OUT32>(m, stream);
             if (e != hipSuccess || (m.split_round == 0 && m.max_half == 0)) return e;
             if (m.host_tiles >= 0 && m.max_half == 0) {   // tiles known on the host: launch the tail only if it has work
                 const long long rem = (long long)m.host_tiles * m.n_tiles % m.split_round;
@@ -798,20 +818,20 @@ hipError_t launch_mode(int block_m, const GemmArgs& a, hipStream_t stream) {
             t.tail = 1;
             // leftover halves (at most split_round) and the half tiles (at most one per group)
             const unsigned grid = (unsigned)m.split_round + (unsigned)m.max_half * (unsigned)m.n_tiles;
-            grouped_gemm_kernel<128, 2, 2, MODE, ABLK><<<grid, kThreads, 0, stream>>>(t);
+            grouped_gemm_kernel<128, 2, 2, MODE, ABLK, OUT32><<<grid, kThreads, 0, stream>>>(t);
             return hipGetLastError();
         }
         case 128: {
             GemmArgs m = a;
             m.split_round = 0;
             m.tail = 0;
-            return launch_cfg<128, 2, 2, MODE, ABLK>(m, stream);
+            return launch_cfg<128, 2, 2, MODE, ABLK, OUT32>(m, stream);
         }
         case 64: {
             GemmArgs m = a;
             m.split_round = 0;
             m.tail = 0;
-            return launch_cfg<64, 1, 4, MODE, ABLK>(m, stream);
+            return launch_cfg<64, 1, 4, MODE, ABLK, OUT32>(m, stream);
         }
         default: return hipErrorInvalidValue;
     }
@@ -820,13 +840,14 @@ hipError_t launch_mode(int block_m, const GemmArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_linear1(int block_m, const GemmArgs& a, hipStream_t stream) {
-    return a.a_blocked ? launch_mode<1, true>(block_m, a, stream) : launch_mode<1, false>(block_m, a, stream);
+    return a.a_blocked ? launch_mode<1, true, false>(block_m, a, stream) : launch_mode<1, false, false>(block_m, a, stream);
 }
 hipError_t launch_linear2(int block_m, const GemmArgs& a, hipStream_t stream) {
-    return launch_mode<2, true>(block_m, a, stream);
+    return a.out_bytes > 0 ? launch_mode<2, true, true>(block_m, a, stream)
+                           : launch_mode<2, true, false>(block_m, a, stream);
 }
 hipError_t launch_gemm_plain(int block_m, const GemmArgs& a, hipStream_t stream) {
-    return launch_mode<3, false>(block_m, a, stream);
+    return launch_mode<3, false, false>(block_m, a, stream);
 }
 hipError_t launch_gemm_splitk(int block_m, const GemmArgs& a, hipStream_t stream) {
     if (a.max_tiles == 0 || a.n_tiles == 0) return hipSuccess;
@@ -835,9 +856,9 @@ hipError_t launch_gemm_splitk(int block_m, const GemmArgs& a, hipStream_t stream
     m.tail = 0;
     const unsigned grid = (unsigned)m.max_tiles * (unsigned)m.n_tiles * (unsigned)m.splits;
     if (block_m == 128)
-        grouped_gemm_kernel<128, 2, 2, 4, false><<<grid, kThreads, 0, stream>>>(m);
+        grouped_gemm_kernel<128, 2, 2, 4, false, false><<<grid, kThreads, 0, stream>>>(m);
     else if (block_m == 64)
-        grouped_gemm_kernel<64, 1, 4, 4, false><<<grid, kThreads, 0, stream>>>(m);
+        grouped_gemm_kernel<64, 1, 4, 4, false, false><<<grid, kThreads, 0, stream>>>(m);
     else
         return hipErrorInvalidValue;
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;

@@ -248,6 +248,9 @@ static int forward_impl(uint16_t* y_bf16, const uint8_t* x_fp8, const uint8_t* x
     a2.stage = reinterpret_cast<uint16_t*>(ws + W.pub.stage);
     a2.topk_weights = topk_weights;
     a2.out_cols = H;
+    // Below 4 GiB of staging rows Linear2 addresses them by 32-bit byte offsets
+    const uint64_t stage_bytes = (uint64_t)T * k * H * sizeof(uint16_t);
+    a2.out_bytes = stage_bytes < (1ull << 32) ? (uint32_t)stage_bytes : 0u;
     if (launch_linear2(BM, a2, stream) != hipSuccess) return MOE_ERR_HIP;
     if (mark(3) != hipSuccess) return MOE_ERR_HIP;
 

@@ -110,6 +110,7 @@ struct GemmArgs {
     uint16_t* stage;
     const float* topk_weights;
     int out_cols;              // = H
+    uint32_t out_bytes;        // bytes of `stage` when below 4 GiB (32-bit store offsets), else 0
     // Split-K of the plain GEMM: `splits` workgroups per output tile, each over ks_split K
     // steps (a multiple of 4), FP32 partials [tile][split][BM][256]
     int splits;

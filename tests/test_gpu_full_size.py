@@ -12,6 +12,9 @@ Each case checks
     minutes, a seeded stratified sample of at least 512 tokens holding at least 8 tokens of
     every non-empty expert, among them its first and its last token (the last one sits in
     that expert's ragged tail tile).
+
+c4_wide is the T=32768 top-8 workload grown to T=40960: its 4.7 GB staging buffer is past
+4 GiB, where Linear2 stores through 64-bit addresses instead of 32-bit buffer offsets.
 """
 import dataclasses
 
@@ -57,15 +60,18 @@ def expert_coverage(idx: np.ndarray, toks, E: int):
     return [(int((sub == e).sum()), int((idx == e).sum())) for e in range(E)]
 
 
+WORKLOADS = dict(CONFIGS, c4_wide=dataclasses.replace(CONFIGS["c4"], name="c4_wide", T=40960))
 # workload -> tokens compared with the oracle (None: all of them)
-FULL = {"c1": None, "c3": None, "c3e": None, "c4": 512, "c2": 512}
+FULL = {"c1": None, "c3": None, "c3e": None, "c4": 512, "c2": 512, "c4_wide": 512}
 PER_EXPERT = 8
 
 
 @pytest.mark.parametrize("name", list(FULL))
 def test_full_size(name):
-    cfg = CONFIGS[name]
+    cfg = WORKLOADS[name]
     print(f"[full] {name}: {cfg}", flush=True)
+    if name == "c4_wide":
+        assert cfg.T * cfg.k * cfg.H * 2 > 1 << 32
     inp = make_inputs(cfg, seed=0, device="cuda")
     run = Run(inp)
     y = run.forward(poison=True)
