@@ -548,7 +548,16 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
     if (ks0 + 6 < nks) step(ks0 + 6, IntC<2>{}, IntC<1>{});
     // the last steps' clamped reloads must land before the slot is reused or the wave ends
     wait_vmem_barrier();
+    // Reads of the accumulators after the last MFMA need wait states, which the s_nop block
+    // gives. The reads are plain register moves that the compiler may hoist above that asm
+    // statement (it did: up to 32 reads, so far only of accumulators a dozen MFMAs old, which
+    // is safe by distance alone); passing every accumulator through an empty asm statement
+    // after it (asm statements keep their order) pins all reads below.
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");   // last MFMA -> reads of acc
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) asm volatile("" : "+a"(acc[fm][fn]));
         // ---- epilogue, in the first A slot (every load has landed) -----------------------
         uint8_t* ep = smem;
         if constexpr (MODE == 1) {

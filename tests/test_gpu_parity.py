@@ -57,6 +57,9 @@ def test_tiny_c0():
     (40, 2, 2, 128, 256, 7),       # H = 128: Linear1 has one K step, Linear2 one half tile
     (1100, 2, 2, 640, 384, 8),     # 256-row tiles and second launch with H = 640
     (300, 4, 3, 128, 128, 9),      # H = I = 128 with rows read through the row list (top-3)
+    (150, 4, 2, 512, 1024, 10),    # 64-row tiles, experts of one and two row tiles, K = 1024
+    (90, 8, 4, 1024, 2048, 11),    # 64-row tiles, rows through the row list (top-4)
+    (12, 24, 1, 1536, 1024, 12),   # mostly empty experts
 ])
 def test_small_shapes(T, E, k, H, I, seed):
     _full_check(MoEConfig("small", T=T, E=E, k=k, H=H, I=I), seed=seed)

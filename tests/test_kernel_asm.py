@@ -7,6 +7,9 @@ kernel's construction promises:
     the 2 wait states such a write needs before an MFMA may read it;
   * the accumulators stay in place: every MFMA's destination equals its accumulator input
     and the K loops move no accumulator (no v_accvgpr_read / write / mov inside a loop);
+  * every read of an accumulator comes at least 19 wait states after the MFMA that last
+    wrote it (the most a 16x16 MFMA's result needs before a VALU may read it), counting
+    every instruction in between, MFMAs included, as one and s_nop N as N + 1;
   * the kernels use no scratch memory inside their K loops.
 """
 import os
@@ -103,6 +106,36 @@ def test_accumulators_stay_tied_and_in_place(asm):
         moves = [l for l in body if l.startswith(("v_accvgpr_read", "v_accvgpr_write", "v_accvgpr_mov"))]
         assert not moves, moves[:4]
         assert not [l for l in body if l.startswith("scratch_")]
-    # Linear1 (A blocked or through the row list), Linear2, plain GEMM: three row-tile classes
-    # each; split-K: two
-    assert n_mfma_loops == 14
+    # Linear1 (A blocked or through the row list), Linear2 (32- or 64-bit stage offsets),
+    # plain GEMM: three row-tile classes each; split-K: two
+    assert n_mfma_loops == 17
+
+
+def _aregs(tok):
+    m = re.match(r"a\[(\d+):(\d+)\]$", tok)
+    if m:
+        return set(range(int(m.group(1)), int(m.group(2)) + 1))
+    m = re.match(r"a(\d+)$", tok)
+    return {int(m.group(1))} if m else set()
+
+
+def test_accumulator_reads_wait_for_their_mfma(asm):
+    checked = 0
+    for i, line in enumerate(asm):
+        if not line.startswith("v_accvgpr_read"):
+            continue
+        src = _aregs(line.split(None, 1)[1].split(",")[1].strip())
+        waits, j = 0, i - 1
+        while j >= 0 and waits < 19:
+            p = asm[j]
+            j -= 1
+            if p.startswith(".Lfunc_end") or p.startswith(".amdhsa_kernel"):
+                break
+            if not _is_instr(p):
+                continue
+            if p.startswith("v_mfma"):
+                assert not (_aregs(_mfma_operands(p)[0]) & src), \
+                    f"{line!r} only {waits} wait states after {p!r}"
+            waits += int(p.split()[1]) + 1 if p.split()[0] == "s_nop" else 1
+        checked += 1
+    assert checked > 1000
