@@ -179,8 +179,11 @@ struct Cfg {
 };
 
 // ABLK: A in the blocked layout (Linear2's h8, Linear1's dispatch copy); otherwise A rows are
-// read through the row list. The forward's GEMMs (MODE 1, 2) read A's scales from the blocked
-// scale copy (h_sf, xg_sf); the plain GEMMs read them row by row.
+// read through the row list. A's scales: Linear2 and Linear1 read the blocked scale copy
+// (h_sf, xg_sf), four fragments' words per 16-byte load, except Linear1's 64-row tiles
+// without a dispatch copy, which read one word per fragment from x_sf through the row list
+// (so a decode needs no gather launch: c1 -1.6 %; with 256-row tiles the per-fragment words
+// cost c3 and c4 3 %). The plain GEMMs read the caller's scale rows likewise.
 template <int BM, int WAVES_M, int WAVES_N, int MODE, bool ABLK, bool OUT32>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args) {
     // The body uses gfx950 buffer descriptors, a device-only type: the host pass of the
@@ -298,7 +301,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
     constexpr bool blocked = ABLK;
     static_assert(!ABLK || MODE <= 2, "blocked A: the forward's GEMMs only");
     static_assert(!OUT32 || MODE == 2, "32-bit output offsets: Linear2 only");
-    constexpr bool sblk = MODE <= 2;   // A scales in the blocked scale layout
+    constexpr bool sblk = MODE == 2 || (MODE == 1 && (ABLK || BM > 64));   // A scales blocked
     static_assert(!sblk || (FM % 4 == 0 && WM % 64 == 0), "scale words of 4 fragments per load");
     const int NKB = args.K / kBK;
     const uint32_t a_kstep = blocked ? (uint32_t)args.hblk * kBK : (uint32_t)kBK;

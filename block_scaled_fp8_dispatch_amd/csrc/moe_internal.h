@@ -73,8 +73,9 @@ struct GemmArgs {
     const uint8_t* a;          // A rows: blocked (h8, or the dispatched x) or x itself
     int a_blocked;             // 1: A blocked like h8; 0 (Linear1 only): rows of x
                                // gathered through perm
-    const uint8_t* a_sf;       // Linear1/2: the blocked scale copy (xg_sf, h_sf), whatever
-                               // a_blocked; plain GEMM: scale rows named by perm
+    const uint8_t* a_sf;       // Linear1/2: the blocked scale copy (xg_sf, h_sf), except
+                               // Linear1 with 64-row tiles and no dispatch copy: x_sf, rows
+                               // named by perm; plain GEMM: scale rows named by perm
     int a_stride;              // bytes per A row (= K)
     int a_sf_stride;           // scale bytes per A row (4*ceil(K/512))
     int K;                     // reduction length (multiple of 128)

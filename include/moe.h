@@ -187,9 +187,11 @@ typedef struct {
                                bytes otherwise: xg == xg_sf): the x row of each padded row's
                                token (zero on padding rows), blocked like h8 with H columns:
                                [P_pad/block_m][H/128][block_m][128] */
-    size_t xg_sf;           /* u8 the scale rows of the dispatched tokens (for every top-k),
-                               4*ceil(H/512) bytes per padded row in the blocked scale layout
-                               of h_sf, zero on padding rows */
+    size_t xg_sf;           /* u8 the scale rows of the dispatched tokens, 4*ceil(H/512)
+                               bytes per padded row in the blocked scale layout of h_sf, zero
+                               on padding rows; written for num_topk <= 2 and for 128- and
+                               256-row tiles (with 64-row tiles and num_topk > 2 Linear1 reads
+                               x_sf through perm and the region is left untouched) */
     size_t total;           /* bytes used */
 } moe_layout_t;
 

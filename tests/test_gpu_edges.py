@@ -179,7 +179,8 @@ def test_dispatch_scale_copy(k, BMexp):
     """The gather's copy of each padded row's token scale row (xg_sf), read back from the
     workspace in the blocked scale layout (decoded by the test's own statement of it): equal
     to the token's x_sf row on every routed row and zero on padding rows, for a top-k with
-    the dispatch copy of x (2) and one without (8)."""
+    the dispatch copy of x (2) and one without (8, 128-row tiles; with 64-row tiles and a
+    top-k above 2 nothing is copied, Linear1 reads x_sf through the row list)."""
     E = 8
     T = 2048 if k == 2 else 160
     cfg = MoEConfig("edge", T=T, E=E, k=k, H=1280, I=256)
