@@ -833,8 +833,12 @@ hipError_t launch_mode(int block_m, const GemmArgs& a, hipStream_t stream) {
             }
             GemmArgs t = m;
             t.tail = 1;
-            // leftover halves (at most split_round) and the half tiles (at most one per group)
-            const unsigned grid = (unsigned)m.split_round + (unsigned)m.max_half * (unsigned)m.n_tiles;
+            // leftover halves (at most split_round) and the half tiles (at most one per group),
+            // which the kernel defers to this launch only where K is long (with short K their
+            // workgroups would all return at once: 896 of them at c3, 3 us)
+            const bool defer_half = !(MODE >= 3 && m.dense_rows > 0) && m.K >= kHalfTileMinK;
+            const unsigned grid = (unsigned)m.split_round + (defer_half ? (unsigned)m.max_half * (unsigned)m.n_tiles : 0u);
+            if (grid == 0) return e;
             grouped_gemm_kernel<128, 2, 2, MODE, ABLK, OUT32><<<grid, kThreads, 0, stream>>>(t);
             return hipGetLastError();
         }
