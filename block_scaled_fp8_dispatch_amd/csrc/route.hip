@@ -119,11 +119,20 @@ __global__ __launch_bounds__(kFusedThreads) void route_fused_kernel(
         for (int w = 0; w < kFusedThreads / 64; ++w) wave_cnt[w][e] = 0;
     }
     if (tid == 0) invalid = 0;
+    // the thread's slots tid, tid + 1024, ..., read once: the scatter below reuses them
+    constexpr int kPer = kFusedMaxSlots / kFusedThreads;
+    int ev[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int s = i * kFusedThreads + tid;
+        ev[i] = s < num_slots ? idx[s] : -1;
+    }
     __syncthreads();
     // histogram and invalid ids
     int my_invalid = 0;
-    for (int s = tid; s < num_slots; s += kFusedThreads) {
-        const int e = idx[s];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int e = ev[i];
         if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
         else if (e != -1) ++my_invalid;
     }
@@ -149,10 +158,13 @@ __global__ __launch_bounds__(kFusedThreads) void route_fused_kernel(
     }
     __syncthreads();
     // stable scatter, 1024 slots per round in slot order
-    for (int s0 = 0; s0 < num_slots; s0 += kFusedThreads) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int s0 = i * kFusedThreads;
+        if (s0 >= num_slots) break;   // uniform
         const int s = s0 + tid;
         const bool in_range = s < num_slots;
-        const int e = in_range ? idx[s] : -1;
+        const int e = ev[i];
         const bool ok = e >= 0 && e < E;
         int rank_w, cnt;
         wave_match(e, ok, nbits, lane, rank_w, cnt);
