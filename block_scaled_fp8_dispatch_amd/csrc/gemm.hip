@@ -178,13 +178,15 @@ struct Cfg {
     static_assert(DA == 2 || (DA == 3 && DB == 3), "issue orders written for these");
 };
 
+// STREAM: B through non-temporal loads (the second launch of the 256-row class: one row tile
+// or one pair of halves per B tile, see kBAux below).
 // ABLK: A in the blocked layout (Linear2's h8, Linear1's dispatch copy); otherwise A rows are
 // read through the row list. A's scales: Linear2 and Linear1 read the blocked scale copy
 // (h_sf, xg_sf), four fragments' words per 16-byte load, except Linear1's 64-row tiles
 // without a dispatch copy, which read one word per fragment from x_sf through the row list
 // (so a decode needs no gather launch: c1 -1.6 %; with 256-row tiles the per-fragment words
 // cost c3 and c4 3 %). The plain GEMMs read the caller's scale rows likewise.
-template <int BM, int WAVES_M, int WAVES_N, int MODE, bool ABLK, bool OUT32>
+template <int BM, int WAVES_M, int WAVES_N, int MODE, bool ABLK, bool OUT32, bool STREAM = false>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args) {
     // The body uses gfx950 buffer descriptors, a device-only type: the host pass of the
     // split compilation sees an empty kernel and emits only its launch stub.
@@ -355,11 +357,14 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs args
         (void*)(args.b_sf + (size_t)expert * args.bs_expert + (size_t)nt * args.bs_ntile +
                 (size_t)(k_begin / 4) * (kBScaleBlockBytes / 4)),
         0, kAllRecords, kRsrcWord3);
-    // 64-row tiles (a few rows per expert, so one row tile reads each weight tile): B data and
-    // scales through non-temporal loads, which stream past the caches (c1: 157 -> 148 us).
-    // Larger classes read each B tile from several row tiles and keep the default policy,
-    // which lets the later reads hit in L2 (non-temporal there: c4 +3.6 %, c2 +0.7 %).
-    constexpr int kBAux = BM == 64 ? 2 : 0;   // cache-policy bits: nt
+    // 64-row tiles (a few rows per expert, so one row tile reads each weight tile) and the
+    // second launch of the 256-row class (its half tiles are one row tile per expert; its
+    // leftover halves run together): B data and scales through non-temporal loads, which
+    // stream past the caches (c1: 157 -> 148 us; second launches: c2 -0.4 %, c3 -0.3 %). The
+    // main launches of the larger classes read each B tile from several row tiles and keep
+    // the default policy, which lets the later reads hit in L2 (non-temporal there: c4
+    // +3.6 %, c2 +0.7 %).
+    constexpr int kBAux = (BM == 64 || STREAM) ? 2 : 0;   // cache-policy bits: nt
     const uint32_t b_voff = (uint32_t)(wave * B_DMA * 1024 + lane * 16);
     const uint32_t bs_voff = (uint32_t)(lane * 4);
 
@@ -852,7 +857,7 @@ hipError_t launch_mode(int block_m, const GemmArgs& a, hipStream_t stream) {
             const bool defer_half = !(MODE >= 3 && m.dense_rows > 0) && m.K >= kHalfTileMinK;
             const unsigned grid = (unsigned)m.split_round + (defer_half ? (unsigned)m.max_half * (unsigned)m.n_tiles : 0u);
             if (grid == 0) return e;
-            grouped_gemm_kernel<128, 2, 2, MODE, ABLK, OUT32><<<grid, kThreads, 0, stream>>>(t);
+            grouped_gemm_kernel<128, 2, 2, MODE, ABLK, OUT32, true><<<grid, kThreads, 0, stream>>>(t);
             return hipGetLastError();
         }
         case 128: {

@@ -107,8 +107,9 @@ def test_accumulators_stay_tied_and_in_place(asm):
         assert not moves, moves[:4]
         assert not [l for l in body if l.startswith("scratch_")]
     # Linear1 (A blocked or through the row list), Linear2 (32- or 64-bit stage offsets),
-    # plain GEMM: three row-tile classes each; split-K: two
-    assert n_mfma_loops == 17
+    # plain GEMM: three row-tile classes each, and a 128-row second-launch kernel each (with
+    # non-temporal B loads); split-K: two
+    assert n_mfma_loops == 22
 
 
 def _aregs(tok):
