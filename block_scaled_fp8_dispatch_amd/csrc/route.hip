@@ -109,6 +109,7 @@ __global__ __launch_bounds__(kFusedThreads) void route_fused_kernel(
     int32_t* __restrict__ perm, int32_t* __restrict__ inv, int32_t* __restrict__ tile_expert,
     int32_t* __restrict__ tile_row0, int max_tiles) {
     __shared__ int hist[kMaxE];                          // then: next row of each expert
+    __shared__ int pad_lo[kMaxE], pad_hi[kMaxE];         // padding rows [lo, hi) of each expert
     __shared__ int wave_cnt[kFusedThreads / 64][kMaxE];
     __shared__ int warp_sums[16];
     __shared__ int invalid;
@@ -148,7 +149,8 @@ __global__ __launch_bounds__(kFusedThreads) void route_fused_kernel(
         counts[tid] = c;
         offsets[tid] = excl;
         if (tid == E - 1) offsets[E] = excl + pad;
-        for (int r = excl + c; r < excl + pad; ++r) perm[r] = -1;
+        pad_lo[tid] = excl + c;
+        pad_hi[tid] = excl + pad;
         hist[tid] = excl;                                // next row of expert tid
     }
     if (tid == 0) {
@@ -157,6 +159,14 @@ __global__ __launch_bounds__(kFusedThreads) void route_fused_kernel(
         meta[2] = block_m;
     }
     __syncthreads();
+    // padding rows of perm set to -1: 1024 / E threads per expert, each taking every
+    // (1024 / E)-th of the expert's padding rows
+    {
+        const int tpe = kFusedThreads / E;
+        const int e = tid / tpe, j = tid % tpe;
+        if (e < E)
+            for (int r = pad_lo[e] + j; r < pad_hi[e]; r += tpe) perm[r] = -1;
+    }
     // stable scatter, 1024 slots per round in slot order
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
@@ -223,8 +233,15 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(
     int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ tile_expert,
     int32_t* __restrict__ tile_row0, int max_tiles) {
     __shared__ int warp_sums[16];
+    __shared__ int pad_lo[kMaxE], pad_hi[kMaxE];   // padding rows [lo, hi) of each expert
+    __shared__ int inv_total;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
+    // invalid ids over all chunks: a strided sum per thread, then atomics in LDS (integer,
+    // so their order does not matter)
+    if (tid == 0) inv_total = 0;
+    int my_inv = 0;
+    for (int b = tid; b < nblk; b += 1024) my_inv += blk_invalid[b];
     int c = 0;
     if (tid < E) {
         // per-chunk bases within the expert, in chunk order (exclusive prefix). The counts of
@@ -256,17 +273,26 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(
     int total = 0;
     for (int w = 0; w < 16; ++w) total += warp_sums[w];
     write_tile_list(tid, E, c, excl, pad, total, block_m, max_tiles, warp_sums, tile_expert, tile_row0, meta);
+    if (my_inv) atomicAdd(&inv_total, my_inv);
     if (tid < E) {
         counts[tid] = c;
         offsets[tid] = excl;
         if (tid == E - 1) offsets[E] = excl + pad;
-        for (int r = excl + c; r < excl + pad; ++r) perm[r] = -1;
+        pad_lo[tid] = excl + c;
+        pad_hi[tid] = excl + pad;
+    }
+    __syncthreads();
+    // padding rows of perm set to -1: 1024 / E threads per expert (E <= 1024), each taking
+    // every (1024 / E)-th of the expert's padding rows
+    {
+        const int tpe = 1024 / E;
+        const int e = tid / tpe, j = tid % tpe;
+        if (e < E)
+            for (int r = pad_lo[e] + j; r < pad_hi[e]; r += tpe) perm[r] = -1;
     }
     if (tid == 0) {
-        int inv = 0;
-        for (int b = 0; b < nblk; ++b) inv += blk_invalid[b];
         meta[0] = total / block_m;
-        meta[1] = inv;
+        meta[1] = inv_total;
         meta[2] = block_m;
     }
 }
@@ -288,10 +314,19 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(
     __syncthreads();
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     const int chunk0 = blockIdx.x * kRouteChunk;
+    // the thread's ids of every round, loaded before the first round (one memory latency,
+    // not one per round)
+    int ev[kSlotsPerThread];
+#pragma unroll
+    for (int round = 0; round < kSlotsPerThread; ++round) {
+        const int s = chunk0 + round * kRouteThreads + tid;
+        ev[round] = s < num_slots ? idx[s] : -1;
+    }
+#pragma unroll
     for (int round = 0; round < kSlotsPerThread; ++round) {
         const int s = chunk0 + round * kRouteThreads + tid;
         const bool in_range = s < num_slots;
-        const int e = in_range ? idx[s] : -1;
+        const int e = ev[round];
         const bool ok = e >= 0 && e < E;
         // lanes of this wave holding the same expert id
         uint64_t peers = __ballot(ok);
