@@ -2,7 +2,8 @@
 
 Edge cases: zero tokens, fewer tokens than the workspace capacity, every slot on one
 expert (with duplicate experts inside a token), k = E, the largest k (64), unused (-1) and
-invalid expert ids with the diagnostic count, many experts with most of them empty.
+invalid expert ids with the diagnostic count (in the one-launch routing and over the chunks
+of the three-launch routing), many experts with most of them empty.
 
 Invariants that hold bit for bit on the GPU, whatever the tolerance against the oracle:
 the same call twice gives the same bytes; permuting tokens permutes y; relabelling
@@ -107,6 +108,31 @@ def test_unused_and_invalid_slots():
     run = Run(inp)
     y, ref, r = _parity(run, inp)
     assert (y[7] == 0).all() and (y[9] == 0).all(), "a token without valid slots is not +0"
+    invalid, counts = moe.moe_read_diagnostics(run.shape, run.ws)
+    assert invalid == int(r["num_invalid"]) == int(((idx < -1) | (idx >= cfg.E)).sum())
+    assert counts == [int(c) for c in r["counts"]]
+
+
+@pytest.mark.parametrize("T,k", [(4097, 1), (2049, 3), (1536, 8)])
+def test_unused_and_invalid_slots_across_chunks(T, k):
+    """The three-launch routing (more than 4096 slots, chunks of 2048): -1 and invalid ids
+    scattered over every chunk, a chunk boundary inside a token's slots, a last chunk of one
+    or three slots (4097 and 6147 slots) or none (12 288): routing bit-exact, parity, and the
+    invalid-id count summed over the chunks."""
+    cfg = MoEConfig("edge", T=T, E=9, k=k, H=256, I=256)
+    print(f"[edge] -1 and invalid ids over chunks {cfg}", flush=True)
+    inp = make_inputs(cfg, seed=31 + k, device="cuda")
+    idx = inp.topk_idx.cpu().numpy().copy()
+    rng = np.random.default_rng(k)
+    idx[rng.random(idx.shape) < 0.1] = -1
+    bad = rng.random(idx.shape) < 0.03
+    idx[bad] = rng.choice(np.array([9, 11, 1000, -2, -9], dtype=np.int64),
+                          size=int(bad.sum())).astype(np.int32)
+    idx[-1, :] = 9                 # the last slot(s), alone in the last chunk, invalid
+    inp = dataclasses.replace(inp, topk_idx=torch.from_numpy(idx).cuda())
+    run = Run(inp)
+    y, ref, r = _parity(run, inp)
+    assert (y[-1] == 0).all(), "a token without valid slots is not +0"
     invalid, counts = moe.moe_read_diagnostics(run.shape, run.ws)
     assert invalid == int(r["num_invalid"]) == int(((idx < -1) | (idx >= cfg.E)).sum())
     assert counts == [int(c) for c in r["counts"]]
