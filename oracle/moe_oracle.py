@@ -37,9 +37,10 @@ once, fp64 -> bf16, round to nearest even.
 Parity pins: every function here is checked in tests/ against library decoders
 (torch float8_e4m3fn / float8_e8m0fnu), exhaustive codebooks, closed-form worked
 examples (tests/golden), exact rational arithmetic, brute force and invariants.
-The remaining unpinned point is fidelity to DeepGEMM's own kernels: the pages
-print no numeric example of the fused operator ("parity unpinned" against the
-upstream library itself).
+Every function is pinned. No pin can reach DeepGEMM's own output: the pages print
+no numeric example of the fused operator, so where they leave a step open the
+readings are checked against their definitions and the mathematics, not against
+upstream numbers.
 """
 from __future__ import annotations
 
